@@ -1,0 +1,178 @@
+/*
+ * decode_attn.h — C ABI of the paged GQA split-KV decode-attention library for MI355X (gfx950).
+ *
+ * What it computes. Single-token decode attention over a paged KV cache for the two layer kinds of
+ * a Gemma-4-style model: "global" layers (every cached key attended; head_dim 512 in Gemma 4) and
+ * "sliding-window" layers (only the last W keys attended; head_dim 256 in Gemma 4). The layer kinds
+ * may differ in head dim, KV-head count and window (Sparse-vLLM PR #27 "feat: support Gemma 4 and
+ * native multimodal inference", section "Gemma 4 文本推理" / Gemma 4 text inference). Several query
+ * heads share one KV head (GQA); one launch handles a whole query-head group (same page, section
+ * "专用算子与性能优化" / dedicated operators). Decode is one new query token per sequence attending
+ * to all of its cached keys (vLLM learning notes "模型库与算子层 — 概念", section "核心操作").
+ *
+ * For sequence b, query head h, KV head g = h / G (G = Hq / Hkv, contiguous groups):
+ *     n   = ctx_lens[b]                      (keys cached for b, the new token included)
+ *     lo  = 0 (global)  or  max(0, n - W) (sliding)
+ *     s_t = scale * <q[b,h,:], K_t>          for t in [lo, n)
+ *     out[b,h,:] = sum_t exp(s_t - m) V_t / sum_t exp(s_t - m),   m = max_t s_t
+ *     lse[b,h]   = m + ln(sum_t exp(s_t - m))
+ * where K_t / V_t live in pool page block_table[b, t / S] at slot t % S. n == 0 gives out = 0 and
+ * lse = -inf.
+ *
+ * How. Split-KV: stage 1 cuts each sequence's key range into num_splits chunks and writes, per
+ * (b, h, split), the chunk's normalised partial output and its log-sum-exp; stage 2 merges the
+ * partials of each (b, h) by their log-sum-exps. The partial buffer reserves one LSE value per
+ * (b, h, split) next to the D partial outputs and is sized once, for the worst case, so that no
+ * call allocates and calls can be captured in a HIP graph (vLLM learning notes, section
+ * "MLA 与 Sparse MLA（DSA）", split-KV MLA decode). A plan is computed on the host from the shape
+ * only; it holds no device pointer, in particular no page-table address, so reusing a plan across
+ * requests with different block tables is always safe (Sparse-vLLM PR #27, section
+ * "专用算子与性能优化", plan invalidation on page-table address change).
+ *
+ * Layouts (all row-major, contiguous, device memory):
+ *     q            [B, Hq, D]             bf16
+ *     k_pool       [P, Hkv, S, D]         bf16   one (page, kv head) block is S*D contiguous values
+ *     v_pool       [P, Hkv, S, D]         bf16
+ *     block_table  [B, max_pages_per_seq] int32  physical page ids; entries of pages holding no key
+ *                                                in [lo, n) are never read and may hold anything
+ *     ctx_lens     [B]                    int32
+ *     out          [B, Hq, D]             fp32
+ *     lse_out      [B, Hq]                fp32   (optional, may be NULL)
+ *     workspace    workspace_bytes bytes  stage-1 partials, see decode_attn_stage1
+ *
+ * Ownership and threading. Every buffer is owned by the caller; the library never allocates or
+ * frees device memory and keeps no mutable global state (a per-device CU count is cached). Calls
+ * are asynchronous on the given stream (a hipStream_t passed as void*, NULL = default stream) and
+ * never synchronise the host, so they can be captured in a HIP graph. Calls that share a
+ * workspace must be ordered on one stream.
+ *
+ * Errors. Every argument is checked on the host before anything is launched; a nonzero
+ * decode_attn_status is returned and nothing is written. DECODE_ATTN_ERR_HIP reports a launch
+ * error. Device-side faults surface at the caller's next synchronisation. On any error the
+ * contents of out / lse_out / workspace are unspecified.
+ *
+ * Robustness inside the kernels: ctx_lens[b] is clamped to [0, max_pages_per_seq * S]; a block
+ * table entry outside [0, P) is never dereferenced and the keys of that page are skipped.
+ */
+#ifndef DECODE_ATTN_H
+#define DECODE_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DECODE_ATTN_OK = 0,
+  DECODE_ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
+  DECODE_ATTN_ERR_SHAPE = 2,       /* inconsistent sizes or values (Hq % Hkv != 0, batch > plan) */
+  DECODE_ATTN_ERR_UNSUPPORTED = 3, /* head_dim, group size or page size with no compiled kernel */
+  DECODE_ATTN_ERR_WORKSPACE = 4,   /* workspace smaller than plan->workspace_bytes */
+  DECODE_ATTN_ERR_PLAN = 5,        /* plan not made by decode_attn_plan, or for the other layer kind */
+  DECODE_ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error (launch or device query) */
+  DECODE_ATTN_ERR_ALIGN = 7        /* q, pools, out or workspace not 16-byte aligned */
+} decode_attn_status;
+
+/* Compiled kernel variants. */
+#define DECODE_ATTN_MAX_SPLITS_LIMIT 1024 /* hard upper bound on num_splits */
+
+/* The shape a plan covers. Values are upper bounds for the calls made with the plan. */
+typedef struct {
+  int32_t batch;             /* B >= 1: most sequences per call */
+  int32_t num_q_heads;       /* Hq >= 1 */
+  int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0; G = Hq / Hkv in {1, 2, 4, 8, 16} */
+  int32_t head_dim;          /* D in {256, 512} */
+  int32_t page_size;         /* S: tokens per page, a multiple of 16, 16 <= S <= 1024 */
+  int32_t max_pages_per_seq; /* columns (row stride) of the block table, >= 1 */
+  int32_t num_pages;         /* P: pages in each pool, >= 1 */
+  int32_t max_ctx_len;       /* longest context expected; sizes the split count only. Longer
+                                contexts are still computed correctly. 0 = max_pages_per_seq * S */
+  int32_t window;            /* 0: global layer; W > 0: sliding layer attending the last W keys */
+  int32_t num_cus;           /* compute units to plan for; 0 = query the current HIP device */
+  int32_t max_splits;        /* cap on num_splits; 0 = library default (256) */
+  int32_t force_splits;      /* 0 = the planner chooses; > 0 = use exactly this many (<= 1024) */
+} decode_attn_problem;
+
+/* A plan: plain data, copy it freely; there is nothing to free. */
+typedef struct {
+  decode_attn_problem problem; /* copy of the problem, num_cus and max_splits resolved */
+  int32_t num_splits;          /* chunks per (sequence, kv head) in stage 1 */
+  int32_t chunk_tokens;        /* tokens per chunk at max_ctx_len (16-token tiles, informational) */
+  int32_t group_size;          /* G = Hq / Hkv */
+  int32_t kind;                /* 1 = global (window == 0), 2 = sliding (window > 0) */
+  uint64_t workspace_bytes;    /* bytes of workspace every call with this plan needs */
+  uint64_t partial_lse_offset; /* byte offset of the LSE plane inside the workspace */
+  uint32_t magic;              /* set by decode_attn_plan; checked by every entry point */
+  int32_t reserved[7];
+} decode_attn_plan_t;
+
+/*
+ * decode_attn_plan — host only, no device work (a device query only when problem->num_cus == 0).
+ * Checks the problem, picks the split count and computes the workspace size.
+ * Split rule: with T = ceil(e / 16) + 1 tiles of 16 keys for the longest attended range
+ * e = min(max_ctx_len, W or unlimited), pairs = batch * Hkv and target = 2 * num_cus workgroups,
+ *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, ceil(T / 8)))
+ * so every chunk holds at least 8 tiles (128 keys) when the context allows it.
+ * Returns DECODE_ATTN_OK, DECODE_ATTN_ERR_NULL, _SHAPE, _UNSUPPORTED or _HIP (device query).
+ */
+int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* plan);
+
+/*
+ * decode_attn_global — attention of a global layer (plan->problem.window == 0): stage 1 then
+ * stage 2 on `stream`. `batch` (0 <= batch <= plan->problem.batch) sequences are computed; batch 0
+ * returns DECODE_ATTN_OK without launching. `scale` multiplies q.k (1/sqrt(D) for Gemma-style
+ * layers). lse_out may be NULL. workspace must hold plan->workspace_bytes.
+ */
+int decode_attn_global(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
+                       int32_t batch, float scale, float* out, float* lse_out, void* workspace,
+                       uint64_t workspace_bytes, void* stream);
+
+/*
+ * decode_attn_sliding — attention of a sliding-window layer: the same call as decode_attn_global
+ * plus `window`, which must equal plan->problem.window (> 0). Only keys t with
+ * max(0, n - window) <= t < n are read; window edges need not fall on 16- or 32-key boundaries
+ * (Sparse-vLLM PR #27, section "专用算子与性能优化", non-32-aligned blocks of the sliding kernel).
+ */
+int decode_attn_sliding(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
+                        int32_t batch, int32_t window, float scale, float* out, float* lse_out,
+                        void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * decode_attn_stage1 — stage 1 alone, for either layer kind (the window comes from the plan).
+ * Writes the workspace, which holds two planes:
+ *     o_part [B, Hq, num_splits, D] fp32 at byte offset 0
+ *     lse    [B, Hq, num_splits]    fp32 at byte offset plan->partial_lse_offset
+ * Split s of sequence b covers the 16-key tiles [floor(s*T_b/ns), floor((s+1)*T_b/ns)) of the
+ * tiles overlapping [lo, n), counted from tile floor(lo/16) (T_b tiles, ns = num_splits); keys
+ * outside [lo, n) are masked. o_part is that chunk's softmax-normalised output and lse its
+ * log-sum-exp of s_t; a chunk with no key has o_part = 0 and lse = -inf. Together with
+ * decode_attn_stage2 this lets the partials be produced and merged separately (for example by
+ * different devices that each own part of the pages).
+ */
+int decode_attn_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
+                       int32_t batch, float scale, void* workspace, uint64_t workspace_bytes,
+                       void* stream);
+
+/*
+ * decode_attn_stage2 — the log-sum-exp merge of the workspace partials written by stage 1:
+ *     M = max_s lse_s,  w_s = exp(lse_s - M),  out = sum_s w_s o_s / sum_s w_s,
+ *     lse_out = M + ln(sum_s w_s);   all lse_s = -inf gives out = 0 and lse_out = -inf.
+ */
+int decode_attn_stage2(const decode_attn_plan_t* plan, int32_t batch, const void* workspace,
+                       uint64_t workspace_bytes, float* out, float* lse_out, void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* decode_attn_status_str(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int decode_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DECODE_ATTN_H */

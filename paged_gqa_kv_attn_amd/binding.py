@@ -1,0 +1,224 @@
+"""ctypes binding of ``libdecode_attn.so`` (declared in ``include/decode_attn.h``).
+
+Argument marshalling only: every step of decode attention runs in the library's HIP kernels.
+Device buffers are passed either as torch CUDA tensors (their ``data_ptr()``) or as raw integer
+device addresses; the stream defaults to torch's current stream. A nonzero status from the
+library raises :class:`DecodeAttnError`. The library is loaded on first use; if it has not been
+built (``python -c "import __graft_entry__ as g; g.build()"``) loading raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libdecode_attn.so"
+_lib = None
+
+PLAN_MAGIC = 0x44415431  # "DAT1", set by decode_attn_plan
+
+STATUS_NAMES = {
+    0: "DECODE_ATTN_OK",
+    1: "DECODE_ATTN_ERR_NULL",
+    2: "DECODE_ATTN_ERR_SHAPE",
+    3: "DECODE_ATTN_ERR_UNSUPPORTED",
+    4: "DECODE_ATTN_ERR_WORKSPACE",
+    5: "DECODE_ATTN_ERR_PLAN",
+    6: "DECODE_ATTN_ERR_HIP",
+    7: "DECODE_ATTN_ERR_ALIGN",
+}
+
+
+class DecodeAttnError(RuntimeError):
+    """A nonzero decode_attn_status returned by the library."""
+
+    def __init__(self, status: int, where: str):
+        self.status = int(status)
+        super().__init__("%s: %s (%d)" % (where, STATUS_NAMES.get(self.status, "unknown"),
+                                          self.status))
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "max_pages_per_seq",
+        "num_pages", "max_ctx_len", "window", "num_cus", "max_splits", "force_splits")]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [
+        ("problem", Problem),
+        ("num_splits", ctypes.c_int32),
+        ("chunk_tokens", ctypes.c_int32),
+        ("group_size", ctypes.c_int32),
+        ("kind", ctypes.c_int32),
+        ("workspace_bytes", ctypes.c_uint64),
+        ("partial_lse_offset", ctypes.c_uint64),
+        ("magic", ctypes.c_uint32),
+        ("reserved", ctypes.c_int32 * 7),
+    ]
+
+    def __repr__(self):
+        p = self.problem
+        return ("Plan(kind=%s, B=%d, Hq=%d, Hkv=%d, D=%d, S=%d, window=%d, num_splits=%d, "
+                "chunk_tokens=%d, workspace_bytes=%d)" % (
+                    {1: "global", 2: "sliding"}.get(self.kind, "?"), p.batch, p.num_q_heads,
+                    p.num_kv_heads, p.head_dim, p.page_size, p.window, self.num_splits,
+                    self.chunk_tokens, self.workspace_bytes))
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+def load_library():
+    """Load ``libdecode_attn.so`` from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError("%s is not built; run __graft_entry__.build() first" % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, u64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float
+    pplan = ctypes.POINTER(Plan)
+    lib.decode_attn_plan.argtypes = [ctypes.POINTER(Problem), pplan]
+    lib.decode_attn_global.argtypes = [pplan, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, u64, vp]
+    lib.decode_attn_sliding.argtypes = [pplan, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp, vp, u64,
+                                        vp]
+    lib.decode_attn_stage1.argtypes = [pplan, vp, vp, vp, vp, vp, i32, f32, vp, u64, vp]
+    lib.decode_attn_stage2.argtypes = [pplan, i32, vp, u64, vp, vp, vp]
+    for fn in ("decode_attn_plan", "decode_attn_global", "decode_attn_sliding",
+               "decode_attn_stage1", "decode_attn_stage2"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.decode_attn_status_str.argtypes = [ctypes.c_int]
+    lib.decode_attn_status_str.restype = ctypes.c_char_p
+    lib.decode_attn_version.argtypes = []
+    lib.decode_attn_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise DecodeAttnError(status, where)
+
+
+def _dev_ptr(x, name: str, dtype=None) -> Optional[int]:
+    """Device address of a torch CUDA tensor (checked) or a raw integer address; None -> NULL."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch CUDA tensor or an integer device address" % name)
+    if not x.is_cuda:
+        raise ValueError("%s must live in device memory" % name)
+    if not x.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and x.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, x.dtype))
+    return x.data_ptr()
+
+
+def _nbytes(x) -> int:
+    return x.numel() * x.element_size()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream  # torch.cuda.Stream
+
+
+def decode_attn_plan(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq,
+                     num_pages, max_ctx_len=0, window=0, num_cus=0, max_splits=0,
+                     force_splits=0) -> Plan:
+    """Host-only planning (see decode_attn_plan in the header). Returns the plan struct."""
+    lib = load_library()
+    prob = Problem(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
+                   int(max_pages_per_seq), int(num_pages), int(max_ctx_len), int(window),
+                   int(num_cus), int(max_splits), int(force_splits))
+    plan = Plan()
+    _check(lib.decode_attn_plan(ctypes.byref(prob), ctypes.byref(plan)), "decode_attn_plan")
+    return plan
+
+
+def _bf16():
+    import torch
+    return torch.bfloat16
+
+
+def _i32():
+    import torch
+    return torch.int32
+
+
+def _f32():
+    import torch
+    return torch.float32
+
+
+def _ws(workspace, workspace_bytes):
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else _nbytes(workspace)
+    return _dev_ptr(workspace, "workspace"), int(workspace_bytes)
+
+
+def decode_attn_global(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, out,
+                       lse_out=None, workspace=None, workspace_bytes=None, stream=None) -> None:
+    lib = load_library()
+    ws, wsb = _ws(workspace, workspace_bytes)
+    _check(lib.decode_attn_global(
+        ctypes.byref(plan), _dev_ptr(q, "q", _bf16()), _dev_ptr(k_pool, "k_pool", _bf16()),
+        _dev_ptr(v_pool, "v_pool", _bf16()), _dev_ptr(block_table, "block_table", _i32()),
+        _dev_ptr(ctx_lens, "ctx_lens", _i32()), int(batch), float(scale),
+        _dev_ptr(out, "out", _f32()), _dev_ptr(lse_out, "lse_out", _f32()), ws, wsb,
+        _stream_handle(stream)), "decode_attn_global")
+
+
+def decode_attn_sliding(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, batch, window, scale,
+                        out, lse_out=None, workspace=None, workspace_bytes=None,
+                        stream=None) -> None:
+    lib = load_library()
+    ws, wsb = _ws(workspace, workspace_bytes)
+    _check(lib.decode_attn_sliding(
+        ctypes.byref(plan), _dev_ptr(q, "q", _bf16()), _dev_ptr(k_pool, "k_pool", _bf16()),
+        _dev_ptr(v_pool, "v_pool", _bf16()), _dev_ptr(block_table, "block_table", _i32()),
+        _dev_ptr(ctx_lens, "ctx_lens", _i32()), int(batch), int(window), float(scale),
+        _dev_ptr(out, "out", _f32()), _dev_ptr(lse_out, "lse_out", _f32()), ws, wsb,
+        _stream_handle(stream)), "decode_attn_sliding")
+
+
+def decode_attn_stage1(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale,
+                       workspace, workspace_bytes=None, stream=None) -> None:
+    lib = load_library()
+    ws, wsb = _ws(workspace, workspace_bytes)
+    _check(lib.decode_attn_stage1(
+        ctypes.byref(plan), _dev_ptr(q, "q", _bf16()), _dev_ptr(k_pool, "k_pool", _bf16()),
+        _dev_ptr(v_pool, "v_pool", _bf16()), _dev_ptr(block_table, "block_table", _i32()),
+        _dev_ptr(ctx_lens, "ctx_lens", _i32()), int(batch), float(scale), ws, wsb,
+        _stream_handle(stream)), "decode_attn_stage1")
+
+
+def decode_attn_stage2(plan: Plan, batch, workspace, out, lse_out=None, workspace_bytes=None,
+                       stream=None) -> None:
+    lib = load_library()
+    ws, wsb = _ws(workspace, workspace_bytes)
+    _check(lib.decode_attn_stage2(
+        ctypes.byref(plan), int(batch), ws, wsb, _dev_ptr(out, "out", _f32()),
+        _dev_ptr(lse_out, "lse_out", _f32()), _stream_handle(stream)), "decode_attn_stage2")
+
+
+def decode_attn_status_str(status: int) -> str:
+    return load_library().decode_attn_status_str(int(status)).decode()
+
+
+def decode_attn_version() -> int:
+    return int(load_library().decode_attn_version())

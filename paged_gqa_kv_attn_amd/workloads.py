@@ -1,0 +1,254 @@
+"""Seeded synthetic workloads for paged decode attention: shapes, page tables and bf16 values.
+
+This module only draws inputs; it contains none of the attention arithmetic, so both the GPU
+tests/benchmark and the CPU oracle can be fed from it. Everything is numpy on the host; values
+are bf16 bit patterns in ``uint16`` arrays.
+
+Workloads follow the serving shapes the pages measure (Gemma 4 26B-A4B decode at 1K to 128K
+input tokens and batch 1 to 8: Sparse-vLLM PR #27 "feat: support Gemma 4 and native multimodal
+inference", section "性能结果" / performance results) with the two Gemma-4 layer kinds (global,
+head_dim 512; sliding window, head_dim 256: same page, section "Gemma 4 文本推理"). No dataset is
+involved; these arrays stand in for the KV caches of those runs.
+
+Structure:
+* pool ``[P, Hkv, S, D]``; a sequence's pages are drawn at random (without replacement) from the
+  pool, so logical neighbours are scattered physically;
+* pool slots that hold no attended key (unused pages, the tail of a partial last page, keys before
+  a sliding window) are filled with a quiet-NaN pattern when ``poison`` is set, so any stray read
+  turns the output into NaN;
+* sliding layers only keep the pages that intersect their window; block-table entries of older
+  pages (and past the last page) are -1.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+BF16_QNAN = 0x7FC0  # quiet NaN bit pattern used to poison unused slots
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); returns uint16 bits."""
+    x = np.asarray(x, dtype=np.float32)
+    u = np.ascontiguousarray(x).view(np.uint32).reshape(x.shape)
+    rounded = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to float32."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+@dataclasses.dataclass(frozen=True)
+class LayerSpec:
+    kind: str            # "global" or "sliding"
+    num_q_heads: int     # Hq
+    num_kv_heads: int    # Hkv
+    head_dim: int        # D
+    window: int = 0      # 0 for global layers
+    q_mult: float = 1.0  # q ~ q_mult * N(0, 1)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int                         # seed root of the workload
+    batch: int
+    ctx: Sequence[int] | str           # fixed lengths, or "ragged" (drawn, see ragged_ctx_lens)
+    layers: Dict[str, LayerSpec]
+    page_size: int = 16
+    num_pages: Optional[int] = None    # pool pages; None = pool_factor * pages needed
+    pool_factor: int = 2
+    description: str = ""
+
+
+def _global(hq: int, hkv: int, q_mult: float = 1.0) -> LayerSpec:
+    return LayerSpec("global", hq, hkv, 512, 0, q_mult)
+
+
+def _sliding(q_mult: float = 1.0) -> LayerSpec:
+    return LayerSpec("sliding", 16, 8, 256, 1024, q_mult)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny_global": Workload(
+        "tiny_global", 0, 1, [1024], {"global": _global(4, 1)}, num_pages=128,
+        description="batch 1, 4 q heads on 1 KV head, D 512, ctx 1024, 64 pages shuffled in a "
+                    "128-page pool"),
+    "short_batch": Workload(
+        "short_batch", 1, 8, [1280] * 8, {"global": _global(16, 2), "sliding": _sliding()},
+        description="batch 8, ctx 1280; global 16/2 heads D 512 and sliding 16/8 heads D 256, W 1024"),
+    "ragged_batch": Workload(
+        "ragged_batch", 2, 8, "ragged", {"global": _global(16, 2), "sliding": _sliding()},
+        description="batch 8, ctx uniform in [3800, 4608] and never a multiple of 32; layers as "
+                    "short_batch"),
+    "long_ctx": Workload(
+        "long_ctx", 3, 4, [32768 + 1024] * 4,
+        {"global": _global(16, 2, q_mult=2.0), "sliding": _sliding(q_mult=2.0)},
+        description="batch 4, ctx 33792; global D 512 GQA 8 and sliding D 256 W 1024; q ~ 2 N(0,1)"),
+    "very_long_b1": Workload(
+        "very_long_b1", 4, 1, [131072 + 1024], {"global": _global(16, 2)}, num_pages=16384,
+        description="batch 1, ctx 132096, global 16/2 heads D 512, 16384-page pool"),
+    "very_long_b2": Workload(
+        "very_long_b2", 5, 2, [65536 + 1024] * 2, {"global": _global(16, 2)}, num_pages=16384,
+        description="batch 2, ctx 66560, global 16/2 heads D 512, 16384-page pool"),
+}
+
+
+def ragged_ctx_lens(rng: np.random.Generator, batch: int, low: int = 3800,
+                    high: int = 4608) -> np.ndarray:
+    """Uniform integer lengths in [low, high], none a multiple of 32, at least one with a partial
+    last page (n % 16 != 0) and one whose 1024-key window starts 16 keys past a 32-key boundary
+    (n % 32 == 16). Draws again until these hold."""
+    while True:
+        n = rng.integers(low, high + 1, size=batch)
+        while np.any(n % 32 == 0):
+            bad = n % 32 == 0
+            n[bad] = rng.integers(low, high + 1, size=int(bad.sum()))
+        if np.any(n % 16 != 0) and np.any(n % 32 == 16):
+            return n.astype(np.int32)
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """Host arrays for one layer call."""
+    q: np.ndarray            # uint16 [B, Hq, D]
+    k_pool: np.ndarray       # uint16 [P, Hkv, S, D]
+    v_pool: np.ndarray       # uint16 [P, Hkv, S, D]
+    block_table: np.ndarray  # int32  [B, max_pages_per_seq]
+    ctx_lens: np.ndarray     # int32  [B]
+    scale: float
+    window: int
+    page_size: int
+
+    @property
+    def dims(self):
+        B, Hq, D = self.q.shape
+        P, Hkv, S, _ = self.k_pool.shape
+        return dict(B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, P=P, M=self.block_table.shape[1])
+
+
+def attended_range(n: int, window: int) -> tuple[int, int]:
+    """Keys [lo, n) a layer reads (used only to decide which pages to allocate and poison)."""
+    return (max(0, n - window) if window > 0 else 0), n
+
+
+def make_layer_inputs(ctx_lens: Sequence[int], num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      page_size: int = 16, window: int = 0, scale: Optional[float] = None,
+                      num_pages: Optional[int] = None, pool_factor: int = 2, q_mult: float = 1.0,
+                      seed=0, poison: bool = True, max_pages_per_seq: Optional[int] = None,
+                      value_dist: str = "normal") -> LayerInputs:
+    """Draw one layer's inputs. ``seed`` is anything ``np.random.SeedSequence`` accepts.
+
+    Pages are allocated only for the logical pages holding attended keys; all other block-table
+    entries are -1. ``value_dist`` "normal" draws N(0,1) values, "zero" leaves them 0."""
+    ctx = np.asarray(ctx_lens, dtype=np.int32)
+    B, S, D = len(ctx), int(page_size), int(head_dim)
+    ss = np.random.SeedSequence(seed)
+    rq, rk, rv, rp = (np.random.default_rng(s) for s in ss.spawn(4))
+
+    ranges = [attended_range(int(n), window) for n in ctx]
+    first = [lo // S for lo, n in ranges]
+    last = [(n - 1) // S if n > 0 else -1 for lo, n in ranges]
+    need = [max(0, l - f + 1) for f, l in zip(first, last)]
+    total = int(sum(need))
+    P = int(num_pages) if num_pages is not None else max(1, pool_factor * total)
+    if P < total:
+        raise ValueError("pool of %d pages cannot hold %d pages" % (P, total))
+    width = max_pages_per_seq or max(1, max((int(n) + S - 1) // S for n in ctx) if B else 1)
+
+    perm = rp.permutation(P).astype(np.int32)
+    table = np.full((B, width), -1, dtype=np.int32)
+    logical = []  # (b, logical page) for each allocated page, in allocation order
+    cursor = 0
+    for b in range(B):
+        for j in range(first[b], last[b] + 1):
+            table[b, j] = perm[cursor]
+            logical.append((b, j))
+            cursor += 1
+    used = perm[:total]
+
+    fill = BF16_QNAN if poison else 0
+    k_pool = np.full((P, num_kv_heads, S, D), fill, dtype=np.uint16)
+    v_pool = np.full((P, num_kv_heads, S, D), fill, dtype=np.uint16)
+    if total:
+        shape = (total, num_kv_heads, S, D)
+        if value_dist == "normal":
+            k_pool[used] = f32_to_bf16_bits(rk.standard_normal(shape, dtype=np.float32))
+            v_pool[used] = f32_to_bf16_bits(rv.standard_normal(shape, dtype=np.float32))
+        elif value_dist == "zero":
+            k_pool[used] = 0
+            v_pool[used] = 0
+        else:
+            raise ValueError(value_dist)
+        if poison:
+            # Slots of allocated pages outside [lo, n): before the window, after the last key.
+            for (b, j), p in zip(logical, used):
+                lo, n = ranges[b]
+                a = max(0, lo - j * S)
+                e = min(S, n - j * S)
+                if a > 0:
+                    k_pool[p, :, :a] = BF16_QNAN
+                    v_pool[p, :, :a] = BF16_QNAN
+                if e < S:
+                    k_pool[p, :, e:] = BF16_QNAN
+                    v_pool[p, :, e:] = BF16_QNAN
+
+    q = f32_to_bf16_bits(np.float32(q_mult) *
+                         rq.standard_normal((B, num_q_heads, D), dtype=np.float32))
+    return LayerInputs(q=q, k_pool=k_pool, v_pool=v_pool, block_table=table, ctx_lens=ctx,
+                       scale=float(scale if scale is not None else 1.0 / math.sqrt(D)),
+                       window=int(window), page_size=S)
+
+
+def workload_ctx_lens(wl: Workload) -> np.ndarray:
+    if isinstance(wl.ctx, str):
+        rng = np.random.default_rng(np.random.SeedSequence([wl.index, 99]))
+        return ragged_ctx_lens(rng, wl.batch)
+    return np.asarray(wl.ctx, dtype=np.int32)
+
+
+def make_workload_layer(name: str, kind: str, poison: bool = True) -> LayerInputs:
+    """Inputs of layer ``kind`` ("global"/"sliding") of workload ``name``; seed = (index, kind)."""
+    wl = WORKLOADS[name]
+    spec = wl.layers[kind]
+    ctx = workload_ctx_lens(wl)
+    seed = [wl.index, 0 if kind == "global" else 1]
+    return make_layer_inputs(ctx, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
+                             page_size=wl.page_size, window=spec.window, scale=spec.scale,
+                             num_pages=wl.num_pages, pool_factor=wl.pool_factor, q_mult=spec.q_mult,
+                             seed=seed, poison=poison)
+
+
+def algorithmic_bytes(ctx_lens: Sequence[int], num_q_heads: int, num_kv_heads: int, head_dim: int,
+                      page_size: int = 16, window: int = 0) -> int:
+    """Bytes the method must move for one layer call: attended K and V (bf16), q (bf16), out
+    (fp32) and the block-table entries of the pages touched (int32)."""
+    kv = 0
+    table = 0
+    for n in ctx_lens:
+        lo, hi = attended_range(int(n), window)
+        e = max(0, hi - lo)
+        kv += e * num_kv_heads * head_dim * 2 * 2
+        if e:
+            table += ((hi - 1) // page_size - lo // page_size + 1) * 4
+    B = len(ctx_lens)
+    return kv + B * num_q_heads * head_dim * 2 + B * num_q_heads * head_dim * 4 + table
+
+
+def algorithmic_flops(ctx_lens: Sequence[int], num_q_heads: int, head_dim: int,
+                      window: int = 0) -> int:
+    """4 * D * Hq flops per attended key (q.k and p.v, multiply and add)."""
+    total = 0
+    for n in ctx_lens:
+        lo, hi = attended_range(int(n), window)
+        total += max(0, hi - lo)
+    return 4 * head_dim * num_q_heads * total
