@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of paged GQA split-KV decode attention on one MI355X.
+
+One step = one decode-attention call of each layer kind of the workload (plan made once, then
+stage 1 + stage 2 of the global layer and the sliding-window layer), with inputs already resident
+in HBM. Default workload: long_ctx (batch 4, 33792 keys per sequence; global layer 16 q / 2 KV
+heads, head_dim 512; sliding layer 16 q / 8 KV heads, head_dim 256, window 1024).
+
+Prints one JSON line: whole-step algorithmic HBM GB/s (value), ms per step, the roofline of the
+dominant kernel (global stage 1: HIP events on its stream around every timed launch), and the fp64
+CPU oracle timed on this host's cores on the same inputs (which also checks the step's outputs).
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attention µs/call and achieved HBM GB/s (% of peak) at 1K–128K ctx"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "paged_gqa_kv_attn_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload: str):
+    """HBM bytes per stage-1 launch from the committed counter summary, if it was taken on the
+    current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", "stage1_global_%s_traffic.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_sources_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="long_ctx")
+    ap.add_argument("--copies", type=int, default=2,
+                    help="distinct copies of the KV pools, used in rotation across steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures a single GPU; --gpus %d is not supported (the decode-attention "
+              "path has no cross-GPU step; run with --gpus 1)" % args.gpus, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 5}), flush=True)
+        return 0
+
+    import paged_gqa_kv_attn_amd as pda
+    from paged_gqa_kv_attn_amd import workloads as wl_mod
+
+    if not os.path.exists(pda.library_path()):
+        from paged_gqa_kv_attn_amd import build
+        build.build()
+    pda.load_library()
+
+    wl = wl_mod.WORKLOADS[args.workload]
+    t_gen = time.time()
+    layers = []
+    for kind in ("global", "sliding"):
+        if kind not in wl.layers:
+            continue
+        inp = wl_mod.make_workload_layer(args.workload, kind)
+        d = inp.dims
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+        k0, v0 = bf(inp.k_pool), bf(inp.v_pool)
+        ks, vs = [k0], [v0]
+        for _ in range(1, max(1, args.copies)):
+            ks.append(k0.clone())
+            vs.append(v0.clone())
+        plan = pda.decode_attn_plan(d["B"], d["Hq"], d["Hkv"], d["D"], d["S"], d["M"], d["P"],
+                                    max_ctx_len=int(inp.ctx_lens.max()), window=inp.window)
+        spec = wl.layers[kind]
+        layers.append(dict(
+            kind=kind, inp=inp, plan=plan, q=bf(inp.q), k=ks, v=vs,
+            bt=torch.from_numpy(inp.block_table).to(dev),
+            ctx=torch.from_numpy(inp.ctx_lens).to(dev),
+            out=torch.empty((d["B"], d["Hq"], d["D"]), device=dev),
+            lse=torch.empty((d["B"], d["Hq"]), device=dev),
+            ws=torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev),
+            bytes=wl_mod.algorithmic_bytes(inp.ctx_lens, spec.num_q_heads, spec.num_kv_heads,
+                                           spec.head_dim, wl.page_size, spec.window),
+            flops=wl_mod.algorithmic_flops(inp.ctx_lens, spec.num_q_heads, spec.head_dim,
+                                           spec.window)))
+        del inp.k_pool, inp.v_pool  # host copies are regenerated for the CPU leg if needed
+    torch.cuda.synchronize()
+    print("# inputs ready in %.1f s: %s" % (time.time() - t_gen, ", ".join(
+        "%s %r" % (L["kind"], L["plan"]) for L in layers)), file=sys.stderr, flush=True)
+
+    dominant = layers[0]  # the global layer's stage 1 moves ~all of the bytes
+    B = dominant["plan"].problem.batch
+
+    def run_layer(L, r, ev_s1=None):
+        p = L["plan"]
+        if L is dominant:
+            if ev_s1 is not None:
+                ev_s1[0].record(stream)
+            pda.decode_attn_stage1(p, L["q"], L["k"][r], L["v"][r], L["bt"], L["ctx"],
+                                   p.problem.batch, L["inp"].scale, L["ws"])
+            if ev_s1 is not None:
+                ev_s1[1].record(stream)
+            pda.decode_attn_stage2(p, p.problem.batch, L["ws"], L["out"], L["lse"])
+        else:
+            pda.decode_attn_sliding(p, L["q"], L["k"][r], L["v"][r], L["bt"], L["ctx"],
+                                    p.problem.batch, p.problem.window, L["inp"].scale, L["out"],
+                                    L["lse"], L["ws"])
+
+    R = len(dominant["k"])
+    for i in range(args.warmup):
+        for L in layers:
+            run_layer(L, i % R)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        for L in layers:
+            run_layer(L, i % R, ev[i] if L is dominant else None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_per_step = (t1 - t0) * 1e3 / K
+    step_bytes = sum(L["bytes"] for L in layers)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    s1_ms = [a.elapsed_time(b) for a, b in ev]
+    s1_avg_us = 1e3 * sum(s1_ms) / len(s1_ms)
+
+    # Algorithmic bytes of one global stage-1 launch: K and V rows of every attended key
+    # (4 * D bytes per key and KV head), q, and the block-table entries of the pages touched.
+    ginp = dominant["inp"]
+    gd = ginp.dims
+    s1_bytes = dominant["bytes"] - gd["B"] * gd["Hq"] * gd["D"] * 4  # minus out (stage 2 writes)
+    achieved = s1_bytes / (s1_avg_us * 1e-6) / 1e9
+    traffic = load_traffic(args.workload)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "description": wl.description,
+            "batch": B,
+            "ctx_lens": [int(x) for x in ginp.ctx_lens],
+            "page_size": wl.page_size,
+            "layers": {L["kind"]: dict(num_q_heads=L["plan"].problem.num_q_heads,
+                                       num_kv_heads=L["plan"].problem.num_kv_heads,
+                                       head_dim=L["plan"].problem.head_dim,
+                                       window=L["plan"].problem.window,
+                                       num_splits=L["plan"].num_splits,
+                                       algorithmic_bytes=L["bytes"]) for L in layers},
+            "step_algorithmic_bytes": step_bytes,
+            "kv_pool_copies_rotated": R,
+        },
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "roofline": {
+            "kernel": "stage1 global (D=%d, G=%d)" % (gd["D"], dominant["plan"].group_size),
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(s1_avg_us, 3),
+            "algorithmic_bytes_per_launch": s1_bytes,
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        host = [wl_mod.make_workload_layer(args.workload, L["kind"]) for L in layers]
+        gpu_out = [(L["out"].cpu().double().numpy(), L["lse"].cpu().double().numpy())
+                   for L in layers]
+        reps, t_cpu, refs = 0, 0.0, None
+        while True:
+            t_a = time.perf_counter()
+            refs = [oracle.decode_attn(h.q, h.k_pool, h.v_pool, h.block_table, h.ctx_lens,
+                                       h.scale, window=h.window) for h in host]
+            t_cpu += time.perf_counter() - t_a
+            reps += 1
+            if t_cpu >= args.cpu_seconds or reps >= 1000:
+                break
+        err = max(float(np.abs(g[0] - r[0]).max()) for g, r in zip(gpu_out, refs))
+        cos = min(float(((g[0] * r[0]).sum(-1) / (np.linalg.norm(g[0], axis=-1) *
+                                                    np.linalg.norm(r[0], axis=-1))).min())
+                  for g, r in zip(gpu_out, refs))
+        cpu_step_s = t_cpu / reps
+        result["cpu_baseline"] = {
+            "value": round(step_bytes / cpu_step_s / 1e9, 3),
+            "unit": "GB/s",
+            "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": "%d full %s steps (all layers), fp64 oracle, %.1f s total" % (
+                reps, args.workload, t_cpu),
+            "us_per_step": round(cpu_step_s * 1e6, 1),
+            "cpu_model": _cpu_model(),
+        }
+        result["parity_vs_oracle"] = {"max_abs_err": err, "min_cos": cos}
+
+    result["kernel_sources_sha256_16"] = kernel_source_hash()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,271 @@
+// decode_attn.cpp — the extern "C" entry points of libdecode_attn.so: planning, host-side argument
+// checks and the two kernel launches. Declared and documented in include/decode_attn.h.
+
+#include "../../include/decode_attn.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace decode_attn {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+int query_num_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DECODE_ATTN_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *cus = cached;
+      return DECODE_ATTN_OK;
+    }
+  }
+  int value = 0;
+  if (hipDeviceGetAttribute(&value, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      value <= 0)
+    return DECODE_ATTN_ERR_HIP;
+  if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(value, std::memory_order_relaxed);
+  *cus = value;
+  return DECODE_ATTN_OK;
+}
+
+uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+// Workspace layout: o_part [B, Hq, ns, D] fp32, then (256-byte aligned) lse [B, Hq, ns] fp32.
+void workspace_layout(const decode_attn_problem& p, int num_splits, uint64_t* lse_offset,
+                      uint64_t* total) {
+  const uint64_t rows = (uint64_t)p.batch * (uint64_t)p.num_q_heads * (uint64_t)num_splits;
+  *lse_offset = align_up(rows * (uint64_t)p.head_dim * 4u, 256);
+  *total = align_up(*lse_offset + rows * 4u, 256);
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+// Checks a plan made by decode_attn_plan and not altered since.
+int check_plan(const decode_attn_plan_t* plan) {
+  if (plan == nullptr) return DECODE_ATTN_ERR_NULL;
+  if (plan->magic != kPlanMagic) return DECODE_ATTN_ERR_PLAN;
+  const decode_attn_problem& p = plan->problem;
+  if (p.batch < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1 ||
+      p.num_q_heads % p.num_kv_heads != 0 || p.page_size < kTile || p.page_size % kTile != 0 ||
+      p.max_pages_per_seq < 1 || p.num_pages < 1 || p.window < 0)
+    return DECODE_ATTN_ERR_PLAN;
+  if (plan->group_size != p.num_q_heads / p.num_kv_heads) return DECODE_ATTN_ERR_PLAN;
+  if (!stage1_supported(p.head_dim, plan->group_size)) return DECODE_ATTN_ERR_PLAN;
+  if (plan->kind != (p.window > 0 ? 2 : 1)) return DECODE_ATTN_ERR_PLAN;
+  if (plan->num_splits < 1 || plan->num_splits > DECODE_ATTN_MAX_SPLITS_LIMIT)
+    return DECODE_ATTN_ERR_PLAN;
+  uint64_t lse_off = 0, total = 0;
+  workspace_layout(p, plan->num_splits, &lse_off, &total);
+  if (plan->workspace_bytes != total || plan->partial_lse_offset != lse_off)
+    return DECODE_ATTN_ERR_PLAN;
+  return DECODE_ATTN_OK;
+}
+
+int check_stage1_args(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
+                      const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
+                      int32_t batch, float scale, const void* workspace,
+                      uint64_t workspace_bytes) {
+  if (batch < 0 || batch > plan->problem.batch) return DECODE_ATTN_ERR_SHAPE;
+  if (!std::isfinite(scale)) return DECODE_ATTN_ERR_SHAPE;
+  if (batch == 0) return DECODE_ATTN_OK;
+  if (!q || !k_pool || !v_pool || !block_table || !ctx_lens || !workspace)
+    return DECODE_ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(workspace, 16) ||
+      !aligned(block_table, 4) || !aligned(ctx_lens, 4))
+    return DECODE_ATTN_ERR_ALIGN;
+  if (workspace_bytes < plan->workspace_bytes) return DECODE_ATTN_ERR_WORKSPACE;
+  return DECODE_ATTN_OK;
+}
+
+int check_stage2_args(const decode_attn_plan_t* plan, int32_t batch, const void* workspace,
+                      uint64_t workspace_bytes, const float* out, const float* lse_out) {
+  if (batch < 0 || batch > plan->problem.batch) return DECODE_ATTN_ERR_SHAPE;
+  if (batch == 0) return DECODE_ATTN_OK;
+  if (!workspace || !out) return DECODE_ATTN_ERR_NULL;
+  if (!aligned(workspace, 16) || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
+    return DECODE_ATTN_ERR_ALIGN;
+  if (workspace_bytes < plan->workspace_bytes) return DECODE_ATTN_ERR_WORKSPACE;
+  return DECODE_ATTN_OK;
+}
+
+int run_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
+               const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
+               int32_t batch, float scale, void* workspace, hipStream_t stream) {
+  const decode_attn_problem& p = plan->problem;
+  Stage1Args a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_pool = static_cast<const uint16_t*>(k_pool);
+  a.v_pool = static_cast<const uint16_t*>(v_pool);
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.o_part = static_cast<float*>(workspace);
+  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->partial_lse_offset);
+  a.num_q_heads = p.num_q_heads;
+  a.num_kv_heads = p.num_kv_heads;
+  a.page_size = p.page_size;
+  a.max_pages_per_seq = p.max_pages_per_seq;
+  a.num_pages = p.num_pages;
+  a.window = p.window;
+  a.num_splits = plan->num_splits;
+  a.scale_log2 = scale * 1.442695040888963407360f;
+  if (launch_stage1(a, p.head_dim, plan->group_size, batch, stream) != hipSuccess)
+    return DECODE_ATTN_ERR_HIP;
+  return DECODE_ATTN_OK;
+}
+
+int run_stage2(const decode_attn_plan_t* plan, int32_t batch, const void* workspace, float* out,
+               float* lse_out, hipStream_t stream) {
+  const decode_attn_problem& p = plan->problem;
+  Stage2Args a;
+  a.o_part = static_cast<const float*>(workspace);
+  a.lse_part =
+      reinterpret_cast<const float*>(static_cast<const char*>(workspace) + plan->partial_lse_offset);
+  a.out = out;
+  a.lse_out = lse_out;
+  a.num_q_heads = p.num_q_heads;
+  a.head_dim = p.head_dim;
+  a.num_splits = plan->num_splits;
+  if (launch_stage2(a, batch, stream) != hipSuccess) return DECODE_ATTN_ERR_HIP;
+  return DECODE_ATTN_OK;
+}
+
+int attend(const decode_attn_plan_t* plan, int expected_kind, const void* q, const void* k_pool,
+           const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens, int32_t batch,
+           float scale, float* out, float* lse_out, void* workspace, uint64_t workspace_bytes,
+           void* stream) {
+  int rc = check_plan(plan);
+  if (rc != DECODE_ATTN_OK) return rc;
+  if (plan->kind != expected_kind) return DECODE_ATTN_ERR_PLAN;
+  rc = check_stage1_args(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, workspace,
+                         workspace_bytes);
+  if (rc != DECODE_ATTN_OK) return rc;
+  rc = check_stage2_args(plan, batch, workspace, workspace_bytes, out, lse_out);
+  if (rc != DECODE_ATTN_OK || batch == 0) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, workspace, s);
+  if (rc != DECODE_ATTN_OK) return rc;
+  return run_stage2(plan, batch, workspace, out, lse_out, s);
+}
+
+}  // namespace
+}  // namespace decode_attn
+
+using namespace decode_attn;
+
+extern "C" {
+
+int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* plan) {
+  if (problem == nullptr || plan == nullptr) return DECODE_ATTN_ERR_NULL;
+  decode_attn_problem p = *problem;
+  if (p.batch < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1 || p.head_dim < 1 ||
+      p.page_size < 1 || p.max_pages_per_seq < 1 || p.num_pages < 1 || p.max_ctx_len < 0 ||
+      p.window < 0 || p.num_cus < 0 || p.max_splits < 0 || p.force_splits < 0)
+    return DECODE_ATTN_ERR_SHAPE;
+  if (p.num_q_heads % p.num_kv_heads != 0) return DECODE_ATTN_ERR_SHAPE;
+  if (p.max_splits > DECODE_ATTN_MAX_SPLITS_LIMIT || p.force_splits > DECODE_ATTN_MAX_SPLITS_LIMIT)
+    return DECODE_ATTN_ERR_SHAPE;
+  if ((int64_t)p.max_pages_per_seq * p.page_size > INT32_MAX) return DECODE_ATTN_ERR_SHAPE;
+  const int G = p.num_q_heads / p.num_kv_heads;
+  if (p.page_size % kTile != 0 || p.page_size > 1024) return DECODE_ATTN_ERR_UNSUPPORTED;
+  if (!stage1_supported(p.head_dim, G)) return DECODE_ATTN_ERR_UNSUPPORTED;
+  if (p.num_cus == 0) {
+    const int rc = query_num_cus(&p.num_cus);
+    if (rc != DECODE_ATTN_OK) return rc;
+  }
+  if (p.max_splits == 0) p.max_splits = kDefaultMaxSplits;
+
+  // Longest key range one sequence can attend, in 16-key tiles (a window may straddle one more).
+  const int64_t max_keys = (int64_t)p.max_pages_per_seq * p.page_size;
+  int64_t e = p.max_ctx_len > 0 ? (p.max_ctx_len < max_keys ? p.max_ctx_len : max_keys) : max_keys;
+  if (p.window > 0 && e > p.window) e = p.window;
+  const int64_t tiles = (e + kTile - 1) / kTile + (p.window > 0 ? 1 : 0);
+  const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
+  const int64_t target = 2 * (int64_t)p.num_cus;
+  int64_t splits = (target + pairs - 1) / pairs;
+  int64_t cap = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
+  if (cap > p.max_splits) cap = p.max_splits;
+  if (cap < 1) cap = 1;
+  if (splits > cap) splits = cap;
+  if (splits < 1) splits = 1;
+  if (p.force_splits > 0) splits = p.force_splits;
+
+  decode_attn_plan_t out = {};
+  out.problem = p;
+  out.num_splits = (int32_t)splits;
+  out.chunk_tokens = (int32_t)(((tiles + splits - 1) / splits) * kTile);
+  out.group_size = G;
+  out.kind = p.window > 0 ? 2 : 1;
+  workspace_layout(p, out.num_splits, &out.partial_lse_offset, &out.workspace_bytes);
+  out.magic = kPlanMagic;
+  *plan = out;
+  return DECODE_ATTN_OK;
+}
+
+int decode_attn_global(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
+                       int32_t batch, float scale, float* out, float* lse_out, void* workspace,
+                       uint64_t workspace_bytes, void* stream) {
+  return attend(plan, 1, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, out, lse_out,
+                workspace, workspace_bytes, stream);
+}
+
+int decode_attn_sliding(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
+                        int32_t batch, int32_t window, float scale, float* out, float* lse_out,
+                        void* workspace, uint64_t workspace_bytes, void* stream) {
+  const int rc = check_plan(plan);
+  if (rc != DECODE_ATTN_OK) return rc;
+  if (plan->kind != 2) return DECODE_ATTN_ERR_PLAN;
+  if (window != plan->problem.window) return DECODE_ATTN_ERR_SHAPE;
+  return attend(plan, 2, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, out, lse_out,
+                workspace, workspace_bytes, stream);
+}
+
+int decode_attn_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
+                       const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
+                       int32_t batch, float scale, void* workspace, uint64_t workspace_bytes,
+                       void* stream) {
+  int rc = check_plan(plan);
+  if (rc != DECODE_ATTN_OK) return rc;
+  rc = check_stage1_args(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, workspace,
+                         workspace_bytes);
+  if (rc != DECODE_ATTN_OK || batch == 0) return rc;
+  return run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, workspace,
+                    static_cast<hipStream_t>(stream));
+}
+
+int decode_attn_stage2(const decode_attn_plan_t* plan, int32_t batch, const void* workspace,
+                       uint64_t workspace_bytes, float* out, float* lse_out, void* stream) {
+  int rc = check_plan(plan);
+  if (rc != DECODE_ATTN_OK) return rc;
+  rc = check_stage2_args(plan, batch, workspace, workspace_bytes, out, lse_out);
+  if (rc != DECODE_ATTN_OK || batch == 0) return rc;
+  return run_stage2(plan, batch, workspace, out, lse_out, static_cast<hipStream_t>(stream));
+}
+
+const char* decode_attn_status_str(int status) {
+  switch (status) {
+    case DECODE_ATTN_OK: return "DECODE_ATTN_OK";
+    case DECODE_ATTN_ERR_NULL: return "DECODE_ATTN_ERR_NULL: a required pointer is NULL";
+    case DECODE_ATTN_ERR_SHAPE: return "DECODE_ATTN_ERR_SHAPE: inconsistent sizes or values";
+    case DECODE_ATTN_ERR_UNSUPPORTED:
+      return "DECODE_ATTN_ERR_UNSUPPORTED: no kernel for this head_dim / group / page size";
+    case DECODE_ATTN_ERR_WORKSPACE: return "DECODE_ATTN_ERR_WORKSPACE: workspace too small";
+    case DECODE_ATTN_ERR_PLAN: return "DECODE_ATTN_ERR_PLAN: invalid plan or wrong layer kind";
+    case DECODE_ATTN_ERR_HIP: return "DECODE_ATTN_ERR_HIP: HIP runtime error";
+    case DECODE_ATTN_ERR_ALIGN: return "DECODE_ATTN_ERR_ALIGN: pointer not aligned";
+    default: return "unknown decode_attn status";
+  }
+}
+
+int decode_attn_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// internal.h — declarations shared by the host entry points and the HIP kernels of
+// libdecode_attn.so. Not part of the public ABI (that is include/decode_attn.h).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace decode_attn {
+
+constexpr uint32_t kPlanMagic = 0x44415431u;  // "DAT1"
+constexpr int kTile = 16;                     // keys per tile: the M dimension of one MFMA
+constexpr int kDefaultMaxSplits = 256;
+constexpr int kMinTilesPerSplit = 8;          // 128 keys
+constexpr int kStage1Threads = 256;           // 4 wavefronts of 64 lanes
+constexpr int kStage2Threads = 256;
+
+// Kernel arguments of stage 1 (one workgroup per (split, kv head, sequence)).
+struct Stage1Args {
+  const uint16_t* q;            // [B, Hq, D] bf16
+  const uint16_t* k_pool;       // [P, Hkv, S, D] bf16
+  const uint16_t* v_pool;       // [P, Hkv, S, D] bf16
+  const int32_t* block_table;   // [B, max_pages_per_seq]
+  const int32_t* ctx_lens;      // [B]
+  float* o_part;                // [B, Hq, num_splits, D]
+  float* lse_part;              // [B, Hq, num_splits]
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+  int32_t window;               // 0 = all keys
+  int32_t num_splits;
+  float scale_log2;             // scale * log2(e): scores in base-2 units
+};
+
+// Kernel arguments of stage 2 (one workgroup per (64-wide slice of D, q head, sequence)).
+struct Stage2Args {
+  const float* o_part;          // [B, Hq, num_splits, D]
+  const float* lse_part;        // [B, Hq, num_splits]
+  float* out;                   // [B, Hq, D]
+  float* lse_out;               // [B, Hq] or nullptr
+  int32_t num_q_heads;
+  int32_t head_dim;
+  int32_t num_splits;
+};
+
+// Launchers (stage1.hip / stage2.hip). They return the launch status and touch nothing else.
+hipError_t launch_stage1(const Stage1Args& args, int head_dim, int group_size, int batch,
+                         hipStream_t stream);
+hipError_t launch_stage2(const Stage2Args& args, int batch, hipStream_t stream);
+
+// True when a stage-1 kernel is compiled for (head_dim, group_size).
+bool stage1_supported(int head_dim, int group_size);
+
+}  // namespace decode_attn

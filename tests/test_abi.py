@@ -1,0 +1,193 @@
+"""The C-ABI library loads, exports every symbol its header declares, plans on the host, and
+rejects bad arguments before launching anything. CPU only: no call here reaches a kernel launch
+or a device query (plans pass num_cus explicitly)."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from paged_gqa_kv_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "decode_attn.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_PLAN, ERR_HIP, ERR_ALIGN = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(decode_attn_\w+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for required in ("decode_attn_plan", "decode_attn_global", "decode_attn_sliding",
+                     "decode_attn_stage1", "decode_attn_stage2", "decode_attn_status_str"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_plan_struct_layout_matches_header():
+    # 12 int32 problem fields, 4 int32, 2 uint64, uint32 magic, 7 int32 reserved (+ padding)
+    assert ctypes.sizeof(binding.Problem) == 48
+    assert binding.Plan.workspace_bytes.offset == 64
+    assert binding.Plan.magic.offset == 80
+    assert ctypes.sizeof(binding.Plan) == 112
+
+
+def plan(**kw):
+    base = dict(batch=4, num_q_heads=16, num_kv_heads=2, head_dim=512, page_size=16,
+                max_pages_per_seq=2112, num_pages=16896, max_ctx_len=33792, window=0,
+                num_cus=256)
+    base.update(kw)
+    return binding.decode_attn_plan(**base)
+
+
+def expected_workspace(B, Hq, ns, D):
+    rows = B * Hq * ns
+    lse_off = -(-rows * D * 4 // 256) * 256
+    return lse_off, -(-(lse_off + rows * 4) // 256) * 256
+
+
+@pytest.mark.parametrize("kw,splits", [
+    (dict(), 64),                                                     # 4 x 33792 global
+    (dict(batch=1, max_pages_per_seq=8256, num_pages=16384, max_ctx_len=132096), 256),
+    (dict(batch=2, max_pages_per_seq=4160, num_pages=16384, max_ctx_len=66560), 128),
+    (dict(batch=8, max_pages_per_seq=80, max_ctx_len=1280), 10),      # capped: >= 8 tiles/split
+    (dict(num_kv_heads=8, head_dim=256, window=1024), 9),             # 65 tiles -> ceil(65/8)
+    (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024), 8),
+])
+def test_plan_split_counts(kw, splits):
+    p = plan(**kw)
+    assert p.num_splits == splits
+    assert p.kind == (2 if p.problem.window else 1)
+    assert p.group_size == p.problem.num_q_heads // p.problem.num_kv_heads
+    off, total = expected_workspace(p.problem.batch, p.problem.num_q_heads, splits,
+                                    p.problem.head_dim)
+    assert p.partial_lse_offset == off and p.workspace_bytes == total
+    assert p.magic == binding.PLAN_MAGIC
+
+
+def test_plan_long_context_split_counts_meet_chunk_rules():
+    # the 32K+ global layers get 16-64 chunks per sequence; the 64K/128K ones >= 128
+    assert 16 <= plan().num_splits <= 64
+    assert plan(batch=1, max_pages_per_seq=8256, num_pages=16384,
+                max_ctx_len=132096).num_splits >= 128
+
+
+def test_plan_force_and_cap():
+    assert plan(force_splits=7).num_splits == 7
+    assert plan(max_splits=5).num_splits == 5
+    assert plan(batch=1, max_ctx_len=16, max_pages_per_seq=1).num_splits == 1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=15), ERR_SHAPE),           # Hq % Hkv
+    (dict(batch=0), ERR_SHAPE),
+    (dict(num_pages=0), ERR_SHAPE),
+    (dict(window=-1), ERR_SHAPE),
+    (dict(force_splits=1025), ERR_SHAPE),
+    (dict(max_splits=2000), ERR_SHAPE),
+    (dict(head_dim=128), ERR_UNSUPPORTED),
+    (dict(num_q_heads=6), ERR_UNSUPPORTED),      # G = 3
+    (dict(num_q_heads=64), ERR_UNSUPPORTED),     # G = 32
+    (dict(page_size=24), ERR_UNSUPPORTED),
+    (dict(page_size=8), ERR_UNSUPPORTED),
+    (dict(page_size=2048, max_pages_per_seq=8), ERR_UNSUPPORTED),
+])
+def test_plan_rejects(kw, status):
+    with pytest.raises(binding.DecodeAttnError) as e:
+        plan(**kw)
+    assert e.value.status == status
+
+
+def test_plan_null_pointers(lib):
+    assert lib.decode_attn_plan(None, None) == ERR_NULL
+
+
+# Fake, aligned, never-dereferenced addresses: every call below must fail validation first.
+A = 1 << 20
+
+
+def call_global(lib, p, q=A, k=A, v=A, bt=A, ctx=A, batch=1, scale=0.1, out=A, lse=None, ws=A,
+                wsb=None):
+    wsb = p.workspace_bytes if wsb is None else wsb
+    return lib.decode_attn_global(ctypes.byref(p), q, k, v, bt, ctx, batch, scale, out, lse, ws,
+                                  wsb, None)
+
+
+def test_entry_validation_before_launch(lib):
+    p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600)
+    assert call_global(lib, p, q=None) == ERR_NULL
+    assert call_global(lib, p, out=None) == ERR_NULL
+    assert call_global(lib, p, ws=None) == ERR_NULL
+    assert call_global(lib, p, q=A + 8) == ERR_ALIGN
+    assert call_global(lib, p, k=A + 2) == ERR_ALIGN
+    assert call_global(lib, p, out=A + 4) == ERR_ALIGN
+    assert call_global(lib, p, bt=A + 1) == ERR_ALIGN
+    assert call_global(lib, p, wsb=p.workspace_bytes - 1) == ERR_WORKSPACE
+    assert call_global(lib, p, batch=3) == ERR_SHAPE
+    assert call_global(lib, p, batch=-1) == ERR_SHAPE
+    assert call_global(lib, p, scale=math.nan) == ERR_SHAPE
+    assert call_global(lib, p, scale=math.inf) == ERR_SHAPE
+    # batch 0 is a no-op: no pointer is needed and nothing is launched
+    assert call_global(lib, p, q=None, k=None, v=None, bt=None, ctx=None, out=None, ws=None,
+                       wsb=0, batch=0) == OK
+
+
+def test_plan_tampering_and_kind(lib):
+    p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600)
+    bad = binding.Plan.from_buffer_copy(p)
+    bad.magic = 0
+    assert call_global(lib, bad) == ERR_PLAN
+    bad = binding.Plan.from_buffer_copy(p)
+    bad.num_splits += 1                        # workspace no longer matches
+    assert call_global(lib, bad) == ERR_PLAN
+    bad = binding.Plan.from_buffer_copy(p)
+    bad.problem.head_dim = 384
+    assert call_global(lib, bad) == ERR_PLAN
+    assert lib.decode_attn_global(None, A, A, A, A, A, 1, 0.1, A, None, A, 1 << 30, None) == \
+        ERR_NULL
+    s = plan(batch=2, num_kv_heads=8, head_dim=256, window=1024, max_pages_per_seq=100,
+             max_ctx_len=1600)
+    assert call_global(lib, s) == ERR_PLAN     # sliding plan on the global entry point
+    args = (A, A, A, A, A, 1)
+    assert lib.decode_attn_sliding(ctypes.byref(p), *args, 1024, 0.1, A, None, A,
+                                   p.workspace_bytes, None) == ERR_PLAN
+    assert lib.decode_attn_sliding(ctypes.byref(s), *args, 512, 0.1, A, None, A,
+                                   s.workspace_bytes, None) == ERR_SHAPE
+
+
+def test_stage_entry_validation(lib):
+    p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600)
+    assert lib.decode_attn_stage1(ctypes.byref(p), A, A, A, A, A, 1, 0.1, None, 0, None) == \
+        ERR_NULL
+    assert lib.decode_attn_stage1(ctypes.byref(p), A, A, A, A, A, 1, 0.1, A, 16, None) == \
+        ERR_WORKSPACE
+    assert lib.decode_attn_stage2(ctypes.byref(p), 1, A, p.workspace_bytes, None, None, None) == \
+        ERR_NULL
+    assert lib.decode_attn_stage2(ctypes.byref(p), 1, A, p.workspace_bytes, A, A + 2, None) == \
+        ERR_ALIGN
+    assert lib.decode_attn_stage2(ctypes.byref(p), 0, None, 0, None, None, None) == OK
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert binding.decode_attn_status_str(code).startswith(binding.STATUS_NAMES[code])
+    assert "unknown" in binding.decode_attn_status_str(99)
+    assert binding.decode_attn_version() >= 100
