@@ -120,7 +120,7 @@ def main() -> int:
                                     max_ctx_len=int(inp.ctx_lens.max()), window=inp.window)
         spec = wl.layers[kind]
         layers.append(dict(
-            kind=kind, inp=inp, plan=plan, q=bf(inp.q), k=ks, v=vs,
+            kind=kind, inp=inp, dims=d, plan=plan, q=bf(inp.q), k=ks, v=vs,
             bt=torch.from_numpy(inp.block_table).to(dev),
             ctx=torch.from_numpy(inp.ctx_lens).to(dev),
             out=torch.empty((d["B"], d["Hq"], d["D"]), device=dev),
@@ -179,7 +179,7 @@ def main() -> int:
     # Algorithmic bytes of one global stage-1 launch: K and V rows of every attended key
     # (4 * D bytes per key and KV head), q, and the block-table entries of the pages touched.
     ginp = dominant["inp"]
-    gd = ginp.dims
+    gd = dominant["dims"]
     s1_bytes = dominant["bytes"] - gd["B"] * gd["Hq"] * gd["D"] * 4  # minus out (stage 2 writes)
     achieved = s1_bytes / (s1_avg_us * 1e-6) / 1e9
     traffic = load_traffic(args.workload)

@@ -7,22 +7,28 @@
 // log-sum-exp, the split-KV partial buffer of vLLM learning notes "模型库与算子层 — 概念",
 // section "MLA 与 Sparse MLA（DSA）".
 //
-// Work decomposition inside a workgroup (4 wavefronts of 64 lanes):
-//   * keys are processed in tiles of 16 (a page of 16 keys, or a 16-key slice of a larger page);
-//     wave w takes tiles w, w+4, ... of the chunk and keeps its own running max / sum / output;
-//   * scores: one v_mfma_f32_16x16x32_bf16 per 32 values of d, A = K tile (16 keys x 32 d, each
-//     lane loads 16 contiguous bytes of one key row straight from HBM), B = q group (32 d x 16
-//     heads, heads >= G zero), read from LDS where the workgroup stored it once;
-//     lane l receives the scores of keys 4*(l/16)..+3 for head l%16;
-//   * softmax: masked keys get -inf by select (never by multiplying a mask, so NaN in unused
-//     slots cannot leak), running max and sum per head in base-2 units with hardware exp2;
-//   * P.V on the vector ALUs: each V row is read with one coalesced 16-byte load per lane (lane l
-//     owns 8 consecutive d), the probabilities of the tile are broadcast through LDS;
-//   * at the end the 4 waves' states are merged in LDS in a fixed order (deterministic).
-// Loads of the next tile are issued as soon as the registers of the current one are consumed
-// (K right after the MFMAs, V right after the P.V update), so one tile half is always in flight.
+// Work decomposition (4 wavefronts of 64 lanes; the chunk is walked in tiles of 16 keys, a page of
+// 16 keys or a 16-key slice of a larger page; all four waves work on the same tile):
+//   * wave w owns the head-dim columns [w*D/4, (w+1)*D/4) of K, V and the output;
+//   * scores: v_mfma_f32_16x16x32_bf16 with A = K tile (16 keys x 32 columns; every lane loads 16
+//     contiguous bytes of one key row straight from HBM) and B = the q group (32 columns x 16
+//     heads, heads >= G zero, kept in registers). Each wave gets the partial scores of its
+//     columns; the four partials meet in LDS (one barrier per tile) and are summed in a fixed
+//     order, so every wave holds the same full scores: lane l has keys 4*(l/16)..+3 of head l%16;
+//   * softmax: keys outside [lo, n) get -inf by select (never by multiplying a mask, so NaN in
+//     unused slots cannot leak), running max and sum per head in base-2 units, hardware exp2;
+//   * P.V: v_mfma_f32_16x16x16_bf16 with A = P (16 heads x 16 keys, which is exactly the layout the
+//     score MFMA left in the lanes, rounded to bf16) and B = V (16 keys x 16 columns). V is loaded
+//     so that lane l holds 16 bytes of keys 4*(l/16)..+3 in its own column slice and is
+//     transposed inside the lane with byte permutes; each wave accumulates O[heads][its columns];
+//   * loads run STAGES tiles ahead in registers: the K registers of a stage are refilled right after
+//     its score MFMAs, the V registers right after its P.V MFMAs.
+// The per-head softmax state is identical in all four waves, so no merge is needed at the end:
+// each wave writes its own columns of the partial output.
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "internal.h"
 
@@ -30,14 +36,13 @@ namespace decode_attn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = kStage1Threads / 64;
 constexpr float kLn2 = 0.693147180559945309417f;
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Read-only kernel inputs (block table, context lengths) are read through the constant address
 // space so uniform indices become scalar loads that do not share the vector-memory counter.
@@ -47,83 +52,62 @@ __device__ __forceinline__ int32_t load_uniform(const int32_t* p, size_t idx) {
   return ((const_i32_ptr)(p))[idx];
 }
 
-// Orders LDS accesses of one wavefront for the compiler; the hardware executes a wave's LDS
-// instructions in issue order, so no wait is needed between lanes of the same wave.
-__device__ __forceinline__ void wave_lds_order() { __asm__ volatile("" ::: "memory"); }
+// Compiler-only ordering of memory accesses (no instruction is emitted).
+__device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
 
-template <int D, int G>
-struct Stage1Shape {
-  static_assert(D == 256 || D == 512, "head_dim");
-  static_assert(G >= 1 && G <= 16, "group size");
-  static constexpr int kSteps = D / 32;                   // MFMA steps over d per tile
-  static constexpr int kLanesPerRow = D / 8;              // lanes covering one V row (16 B each)
-  static constexpr int kRowsPerLoad = 64 / kLanesPerRow;  // V rows per wave-wide load
-  static constexpr int kVLoads = kTile / kRowsPerLoad;    // V loads per tile
-  static constexpr int kHeadChunk = (D == 512) ? (G < 4 ? G : 4) : (G < 8 ? G : 8);
-  // LDS: q operand + per-wave probability tiles during the key loop; merge slices afterwards.
-  static constexpr int kQBytes = kSteps * 64 * 16;
-  static constexpr int kPRowFloats = 16;                  // one row per key of the tile
-  static constexpr int kPBytes = kWaves * (kTile + 1) * kPRowFloats * 4;  // + alpha row
-  static constexpr int kMergeBytes = kWaves * kHeadChunk * D * 4;
-  static constexpr int kLoopBytes = kQBytes + kPBytes;
-  static constexpr int kUnionBytes = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
-};
-
-// acc[h][:] += p[h][key] * V[key][lane's 8 d] for the keys of one tile. MASKED: keys outside
-// [key_lo, key_hi) have V replaced by 0 (their p is already 0; 0 * NaN would not be).
-template <int D, int G, bool MASKED>
-__device__ __forceinline__ void pv_update(float (&acc)[G][8],
-                                          const u32x4 (&vreg)[Stage1Shape<D, G>::kVLoads],
-                                          const float* p_lds, int v_row, int tok0, int key_lo,
-                                          int key_hi) {
-  using Sh = Stage1Shape<D, G>;
-#pragma unroll
-  for (int i = 0; i < Sh::kVLoads; ++i) {
-    const int kr = i * Sh::kRowsPerLoad + v_row;
-    float pv[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) pv[h] = p_lds[kr * 16 + h];
-    const u32x4 w = vreg[i];
-    float v[8] = {bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1]),
-                  bf16_lo(w[2]), bf16_hi(w[2]), bf16_lo(w[3]), bf16_hi(w[3])};
-    if (MASKED) {
-      const int t = tok0 + kr;
-      const bool valid = t >= key_lo && t < key_hi;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = valid ? v[e] : 0.f;
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(pv[h], v[e], acc[h][e]);
-    // Keep the scheduler from hoisting every row's reads and conversions at once.
-    if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-  }
+// Workgroup barrier that waits for this wave's LDS accesses only (s_waitcnt lgkmcnt(0)), leaving
+// outstanding global loads in flight.
+__device__ __forceinline__ void lds_barrier() {
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // vmcnt = max, expcnt = max, lgkmcnt = 0
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(kStage1Threads) void stage1_kernel(const Stage1Args a) {
-  using Sh = Stage1Shape<D, G>;
-  constexpr int kSteps = Sh::kSteps;
-  constexpr int kVLoads = Sh::kVLoads;
-  constexpr int kRowsPerLoad = Sh::kRowsPerLoad;
-  constexpr int kLanesPerRow = Sh::kLanesPerRow;
-  constexpr int kHC = Sh::kHeadChunk;
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
 
-  __shared__ __attribute__((aligned(16))) float ml_lds[kWaves][16][2];
-  __shared__ __attribute__((aligned(16))) unsigned char smem[Sh::kUnionBytes];
-  u32x4* q_lds = reinterpret_cast<u32x4*>(smem);
-  float* p_lds_all = reinterpret_cast<float*>(smem + Sh::kQBytes);
-  float* merge_lds = reinterpret_cast<float*>(smem);
+template <int D>
+struct Shape {
+  static_assert(D == 256 || D == 512, "head_dim");
+  static constexpr int kCols = D / kWaves;    // columns per wave
+  static constexpr int kKSteps = kCols / 32;  // score MFMAs per tile per wave
+  static constexpr int kVE = kCols / 16;      // columns per lane in a V row (8 or 4)
+  static constexpr int kVDwords = kVE / 2;    // dwords per lane per V row
+};
+
+template <int D>
+using VRow = typename std::conditional<Shape<D>::kVDwords == 4, u32x4, u32x2>::type;
+
+// One step's worth of this wave's slice of K and V: SUB tiles of 16 keys.
+template <int D, int SUB>
+struct StepRegs {
+  bf16x8 k[SUB][Shape<D>::kKSteps];
+  VRow<D> v[SUB][4];  // tile u, keys 4*(lane/16)+i, i = 0..3
+};
+
+template <int D, int G, int SUB>
+__global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1Args a) {
+  using Sh = Shape<D>;
+  constexpr int kKSteps = Sh::kKSteps;
+  constexpr int kVE = Sh::kVE;
+
+  __shared__ __attribute__((aligned(16))) f32x4 score_lds[2][SUB][kWaves][64];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = lane >> 4;  // lane group 0..3
+  const int col = lane & 15;  // column (scores: head; P.V: column block)
   const int S = a.page_size;
-  const int Hkv = a.num_kv_heads;
   const int ns = a.num_splits;
+  const int c0 = wave * Sh::kCols;  // first head-dim column of this wave
+  const size_t row0 = (size_t)b * a.num_q_heads + (size_t)kvh * G;
 
   // Key range of this sequence and the tiles of this split.
   const int max_keys = a.max_pages_per_seq * S;
@@ -136,207 +120,240 @@ __global__ __launch_bounds__(kStage1Threads) void stage1_kernel(const Stage1Args
   const int t_begin = tile_lo + (int)(((int64_t)split * T) / ns);
   const int t_end = tile_lo + (int)(((int64_t)(split + 1) * T) / ns);
   const int tiles_per_page = S / kTile;
+  const size_t table_row = (size_t)b * a.max_pages_per_seq;
 
-  // q group -> LDS in MFMA B-operand order: entry (j, l) = q[h = l%16][j*32 + (l/16)*8 .. +8].
-  const uint16_t* qg = a.q + ((size_t)b * a.num_q_heads + (size_t)kvh * G) * D;
-  for (int idx = threadIdx.x; idx < kSteps * 64; idx += kStage1Threads) {
-    const int j = idx >> 6, l = idx & 63, h = l & 15;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (h < G) v = *reinterpret_cast<const u32x4*>(qg + h * D + j * 32 + (l >> 4) * 8);
-    q_lds[idx] = v;
+  if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
+    for (int idx = lane; idx < G * Sh::kCols; idx += 64) {
+      const int h = idx / Sh::kCols;
+      a.o_part[((row0 + h) * ns + split) * D + c0 + (idx - h * Sh::kCols)] = 0.f;
+    }
+    if (wave == 0 && lane < G) a.lse_part[(row0 + lane) * ns + split] = -INFINITY;
+    return;
   }
-  __syncthreads();
+  const int t_last = t_end - 1;
 
-  float* p_lds = p_lds_all + wave * (kTile + 1) * Sh::kPRowFloats;
-  const bf16x8* q_op = reinterpret_cast<const bf16x8*>(q_lds) + lane;
-
-  // Per-lane pointers inside a 16-key tile (element offsets from the tile base).
-  const int k_lane_off = (lane & 15) * D + (lane >> 4) * 8;
-  const int v_row = lane / kLanesPerRow;
-  const int v_lane_off = v_row * D + (lane % kLanesPerRow) * 8;
-
-  float m_run = -INFINITY;  // running max (base-2 units) of head lane%16
-  float l_run = 0.f;        // running sum of exp2(s - m_run) of head lane%16
-  float acc[G][8];
+  // q group, B operand of the score MFMA: q[h = col][c0 + 32*j + 8*grp .. +8], zero for h >= G.
+  // Every lane loads (a clamped row) so no load sits under a divergent branch.
+  bf16x8 qop[kKSteps];
+  {
+    const uint16_t* qg = a.q + row0 * D;
+    const int hq = col < G ? col : G - 1;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+    for (int j = 0; j < kKSteps; ++j) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qg + hq * D + c0 + 32 * j + 8 * grp);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qop[j] = __builtin_bit_cast(bf16x8, col < G ? v : z);
+    }
+  }
 
-  bf16x8 kreg[kSteps];
-  u32x4 vreg[kVLoads];
+  // Per-lane element offsets inside a tile: K (A operand) row = col, columns c0 + 32j + 8grp;
+  // V rows 4grp + i, columns c0 + kVE*col .. + kVE.
+  const int k_off = col * D + c0 + 8 * grp;
+  const int v_off = (4 * grp) * D + c0 + kVE * col;
 
-  // Tile -> (element offset of the tile in the pools, page valid).
+  // Tile -> element offset of its first key in the pools. Tiles past the split re-read its last
+  // tile (an L2 hit; they are masked) so every load is unconditional and the compiler can count
+  // outstanding loads exactly. Invalid page ids are never dereferenced: page 0 is read instead
+  // and the tile is masked.
   auto tile_base = [&](int ti, bool& ok) -> size_t {
-    const int col = ti / tiles_per_page;
-    int phys = load_uniform(a.block_table, (size_t)b * a.max_pages_per_seq + col);
-    ok = (unsigned)phys < (unsigned)a.num_pages;
-    phys = ok ? phys : 0;  // never dereference an invalid id; the tile is masked instead
-    const int off = (ti - col * tiles_per_page) * kTile;
-    return (((size_t)phys * Hkv + kvh) * S + off) * D;
+    const int tc = ti < t_end ? ti : t_last;
+    const int pc = tc / tiles_per_page;
+    int phys = load_uniform(a.block_table, table_row + pc);
+    ok = ti < t_end && (unsigned)phys < (unsigned)a.num_pages;
+    phys = (unsigned)phys < (unsigned)a.num_pages ? phys : 0;
+    return (((size_t)phys * a.num_kv_heads + kvh) * S + (tc - pc * tiles_per_page) * kTile) * D;
   };
 
-  int ti = t_begin + wave;
-  bool ok = false;
-  size_t base = 0;
-  if (ti < t_end) {
-    base = tile_base(ti, ok);
-    const uint16_t* kp = a.k_pool + base + k_lane_off;
-    const uint16_t* vp = a.v_pool + base + v_lane_off;
+  StepRegs<D, SUB> r;
+  size_t base[SUB];
+  bool ok[SUB];
 #pragma unroll
-    for (int j = 0; j < kSteps; ++j) kreg[j] = *reinterpret_cast<const bf16x8*>(kp + j * 32);
+  for (int u = 0; u < SUB; ++u) base[u] = tile_base(t_begin + u, ok[u]);
 #pragma unroll
-    for (int i = 0; i < kVLoads; ++i)
-      vreg[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)i * kRowsPerLoad * D);
-  }
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int j = 0; j < kKSteps; ++j)
+      r.k[u][j] = *reinterpret_cast<const bf16x8*>(a.k_pool + base[u] + k_off + 32 * j);
+#pragma unroll
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r.v[u][i] = *reinterpret_cast<const VRow<D>*>(a.v_pool + base[u] + v_off + i * D);
+  // A fence the loop latch does not have: otherwise the identical trailing V loads of this
+  // prologue and of the loop body get merged into the loop header, which would turn the V
+  // prefetch into a load at the top of every step.
+  __asm__ volatile("; stage-1 prologue loads issued" ::: "memory");
 
-  while (ti < t_end) {
-    // Scores of the 16 keys for the 16 (padded) heads; two accumulators shorten the chain.
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running max (base-2 units) of head `col`
+  float l_run = 0.f;        // running sum of exp2(s - m_run) of head `col`
+  f32x4 acc[kVE];           // O[head 4*grp + r][column c0 + kVE*col + e] = acc[e][r]
 #pragma unroll
-    for (int j = 0; j < kSteps; j += 2) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[j], q_op[j * 64], s0, 0, 0, 0);
-      if (j + 1 < kSteps)
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[j + 1], q_op[(j + 1) * 64], s1, 0, 0, 0);
+  for (int e = 0; e < kVE; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int buf = 0;
+  for (int t0 = t_begin; t0 < t_end; t0 += SUB) {
+    // Partial scores of this wave's columns for the SUB tiles of the step.
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < kKSteps; j += 2) {
+        p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[u][j], qop[j], p0, 0, 0, 0);
+        if (j + 1 < kKSteps)
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[u][j + 1], qop[j + 1], p1, 0, 0, 0);
+      }
+      score_lds[buf][u][wave][lane] = p0 + p1;
     }
 
-    const int tn = ti + kWaves;
-    const bool has_next = tn < t_end;
-    bool ok_next = false;
-    size_t base_next = 0;
-    if (has_next) {
-      base_next = tile_base(tn, ok_next);
-      const uint16_t* kp = a.k_pool + base_next + k_lane_off;
+    // Next step's K into the registers just consumed. The scheduling barriers keep loads in
+    // program order (K of step i+1 before V of step i+1), which the wait counts rely on.
+    __builtin_amdgcn_sched_barrier(0);
+    const int tn = t0 + SUB;
+    bool ok_n[SUB];
+    size_t base_n[SUB];
 #pragma unroll
-      for (int j = 0; j < kSteps; ++j) kreg[j] = *reinterpret_cast<const bf16x8*>(kp + j * 32);
-    }
+    for (int u = 0; u < SUB; ++u) base_n[u] = tile_base(tn + u, ok_n[u]);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int j = 0; j < kKSteps; ++j)
+        r.k[u][j] = *reinterpret_cast<const bf16x8*>(a.k_pool + base_n[u] + k_off + 32 * j);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // Mask and online softmax for head lane%16.
-    const int tok0 = ti * kTile;
-    const int key_lo = ok ? (lo > tok0 ? lo : tok0) : tok0;
-    const int key_hi = ok ? (n < tok0 + kTile ? n : tok0 + kTile) : tok0;
-    const bool full = key_lo == tok0 && key_hi == tok0 + kTile;
-    float sc[4];
+    lds_barrier();
+    f32x4 sc[SUB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = tok0 + 4 * (lane >> 4) + r;
-      const float raw = s0[r] + s1[r];
-      sc[r] = (t >= key_lo && t < key_hi) ? raw * a.scale_log2 : -INFINITY;
+    for (int u = 0; u < SUB; ++u) {
+      sc[u] = score_lds[buf][u][0][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) sc[u] += score_lds[buf][u][w][lane];
     }
-    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    buf ^= 1;
+
+    // Mask and online softmax for head `col` over the SUB*16 keys of the step.
+    int key_lo[SUB], key_hi[SUB];
+    bool full = true;
+    float mt = -INFINITY;
+    float s2[SUB][4];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const int tok0 = (t0 + u) * kTile;
+      key_lo[u] = ok[u] ? (lo > tok0 ? lo : tok0) : tok0;
+      key_hi[u] = ok[u] ? (n < tok0 + kTile ? n : tok0 + kTile) : tok0;
+      full = full && key_lo[u] == tok0 && key_hi[u] == tok0 + kTile;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tok0 + 4 * grp + i;
+        s2[u][i] = (t >= key_lo[u] && t < key_hi[u]) ? sc[u][i] * a.scale_log2 : -INFINITY;
+        mt = fmaxf(mt, s2[u][i]);
+      }
+    }
     mt = fmaxf(mt, __shfl_xor(mt, 16));
     mt = fmaxf(mt, __shfl_xor(mt, 32));
     const float m_new = fmaxf(m_run, mt);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(sc[r] - m_use);
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float ps = (p[0] + p[1]) + (p[2] + p[3]);
+    float ps = 0.f;
+    i16x4 pop[SUB];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s2[u][i] - m_use);
+      ps += (p[0] + p[1]) + (p[2] + p[3]);
+      // P as the A operand: P[head col][keys 4*grp .. +3 of tile u] in bf16.
+      const u32x2 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+      pop[u] = __builtin_bit_cast(i16x4, pa);
+    }
     ps += __shfl_xor(ps, 16);
     ps += __shfl_xor(ps, 32);
     l_run = l_run * alpha + ps;
     m_run = m_new;
 
-    // Broadcast the probabilities (key-major, 16 heads per row) and the rescale factors.
+    // Rescale the accumulator rows (heads 4*grp + r) when some running max moved.
+    if (__any(alpha != 1.f)) {
+      float al[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p_lds[(4 * (lane >> 4) + r) * 16 + (lane & 15)] = p[r];
-    if (lane < 16) p_lds[kTile * 16 + lane] = alpha;
-    wave_lds_order();
-
-    if (__any(lane < G && alpha != 1.f)) {  // skip when no running max moved
-      float al[G];
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
 #pragma unroll
-      for (int h = 0; h < G; ++h) al[h] = p_lds[kTile * 16 + h];
+      for (int e = 0; e < kVE; ++e)
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+        for (int i = 0; i < 4; ++i) acc[e][i] *= al[i];
     }
 
-    // P.V: lane owns d = (lane % kLanesPerRow)*8 .. +8 of key row i*kRowsPerLoad + v_row.
-    if (full)
-      pv_update<D, G, false>(acc, vreg, p_lds, v_row, 0, 0, 0);
-    else
-      pv_update<D, G, true>(acc, vreg, p_lds, v_row, tok0, key_lo, key_hi);
-    wave_lds_order();
-
-    if (has_next) {
-      const uint16_t* vp = a.v_pool + base_next + v_lane_off;
+    // P.V, one tile at a time.
 #pragma unroll
-      for (int i = 0; i < kVLoads; ++i)
-        vreg[i] = *reinterpret_cast<const u32x4*>(vp + (size_t)i * kRowsPerLoad * D);
+    for (int u = 0; u < SUB; ++u) {
+      VRow<D> vr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vr[i] = r.v[u][i];
+      if (!full) {  // masked keys: V := 0 (their p is 0, but 0 * NaN would not be)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = (t0 + u) * kTile + 4 * grp + i;
+          const bool valid = t >= key_lo[u] && t < key_hi[u];
+#pragma unroll
+          for (int d = 0; d < Sh::kVDwords; ++d) vr[i][d] = valid ? vr[i][d] : 0u;
+        }
+      }
+      // Transpose in the lane: B operand e = V[keys 4*grp + 0..3][column kVE*col + e].
+#pragma unroll
+      for (int d = 0; d < Sh::kVDwords; ++d) {
+        const u32x2 be = {__builtin_amdgcn_perm(vr[1][d], vr[0][d], 0x05040100u),
+                          __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x05040100u)};
+        const u32x2 bo = {__builtin_amdgcn_perm(vr[1][d], vr[0][d], 0x07060302u),
+                          __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x07060302u)};
+        acc[2 * d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            pop[u], __builtin_bit_cast(i16x4, be), acc[2 * d], 0, 0, 0);
+        acc[2 * d + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            pop[u], __builtin_bit_cast(i16x4, bo), acc[2 * d + 1], 0, 0, 0);
+      }
     }
-    ti = tn;
-    ok = ok_next;
-    base = base_next;
+
+    // Next step's V into the registers just consumed.
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r.v[u][i] = *reinterpret_cast<const VRow<D>*>(a.v_pool + base_n[u] + v_off + i * D);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) ok[u] = ok_n[u];
   }
-  (void)base;
 
-  // Lanes that covered different key rows of the same d fold their sums (same running max).
+  // Normalise and write this wave's columns of the partial output; lane holds heads 4*grp + i.
 #pragma unroll
-  for (int step = kLanesPerRow; step < 64; step *= 2)
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] += __shfl_xor(acc[h][e], step);
-
-  if (lane < 16) {
-    ml_lds[wave][lane][0] = m_run;
-    ml_lds[wave][lane][1] = l_run;
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * grp + i;
+    const float lh = __shfl(l_run, h);
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    if (h < G) {
+      float* dst = a.o_part + ((row0 + h) * ns + split) * D + c0 + kVE * col;
+      if constexpr (kVE == 8) {
+        const f32x4 lo4 = {acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
+        const f32x4 hi4 = {acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv, acc[7][i] * inv};
+        reinterpret_cast<f32x4*>(dst)[0] = lo4;
+        reinterpret_cast<f32x4*>(dst)[1] = hi4;
+      } else {
+        const f32x4 v4 = {acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
+        reinterpret_cast<f32x4*>(dst)[0] = v4;
+      }
+    }
   }
-  __syncthreads();  // ml visible; q/p regions free for the merge slices
-
-  // Per head: overall max M, overall sum L, and this wave's weight exp2(m_w - M) / L.
-  const size_t row0 = (size_t)b * a.num_q_heads + (size_t)kvh * G;
-  float* o_dst = a.o_part;
-#pragma unroll
-  for (int hc = 0; hc < G; hc += kHC) {
-#pragma unroll
-    for (int hh = 0; hh < kHC; ++hh) {
-      const int h = hc + hh;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml_lds[w][h][0]);
-      float L = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = ml_lds[w][h][0];
-        L += (mw == -INFINITY) ? 0.f : ml_lds[w][h][1] * __builtin_amdgcn_exp2f(mw - M);
-      }
-      const float mine = ml_lds[wave][h][0];
-      const float f = (mine == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mine - M) / L;
-      if (lane < kLanesPerRow) {
-        float* dst = merge_lds + ((wave * kHC + hh) * D + lane * 8);
-        f32x4 lo4 = {acc[h][0] * f, acc[h][1] * f, acc[h][2] * f, acc[h][3] * f};
-        f32x4 hi4 = {acc[h][4] * f, acc[h][5] * f, acc[h][6] * f, acc[h][7] * f};
-        *reinterpret_cast<f32x4*>(dst) = lo4;
-        *reinterpret_cast<f32x4*>(dst + 4) = hi4;
-      }
-      if (threadIdx.x == 0) {
-        const float lse = (M == -INFINITY) ? -INFINITY : (M + __log2f(L)) * kLn2;
-        a.lse_part[(row0 + h) * ns + split] = lse;
-      }
-    }
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < kHC * D; idx += kStage1Threads) {
-      const int hh = idx / D, d = idx - hh * D;
-      float o = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) o += merge_lds[(w * kHC + hh) * D + d];
-      o_dst[((row0 + hc + hh) * ns + split) * D + d] = o;
-    }
-    __syncthreads();
+  if (wave == 0 && lane < G) {
+    const float lse = (m_run == -INFINITY) ? -INFINITY : (m_run + __log2f(l_run)) * kLn2;
+    a.lse_part[(row0 + lane) * ns + split] = lse;
   }
 }
 
 template <int D, int G>
 hipError_t launch(const Stage1Args& args, int batch, hipStream_t stream) {
+  constexpr int kSub = 4;  // tiles of 16 keys per loop step
   dim3 grid(args.num_splits, args.num_kv_heads, batch);
   dim3 block(kStage1Threads);
   void* kargs[] = {const_cast<Stage1Args*>(&args)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stage1_kernel<D, G>), grid, block, kargs,
-                         0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub>), grid,
+                         block, kargs, 0, stream);
 }
 
 template <int D>

@@ -64,8 +64,12 @@ def test_forced_split_counts_agree():
         out, lse = gu.run(inp, force_splits=ns)
         gu.compare(out, lse, *ref, "splits=%d" % ns)
         outs.append(out)
+    # P is rounded to bf16 before P.V (relative error <= 2^-9 per weight). Different split
+    # counts subtract different running maxima, so the roundings differ and two results may
+    # differ by up to about 2 * 2^-9 * max|V| (~1.6e-2 for |V| <= 4); each one already meets the
+    # oracle bar above, so require mutual agreement at that bar.
     for o in outs[1:]:
-        np.testing.assert_allclose(o, outs[0], atol=2e-5, rtol=0)
+        np.testing.assert_allclose(o, outs[0], atol=gu.MAX_ABS, rtol=0)
 
 
 def test_page_permutation_is_bitwise_invariant():
