@@ -110,10 +110,13 @@ typedef struct {
 /*
  * decode_attn_plan — host only, no device work (a device query only when problem->num_cus == 0).
  * Checks the problem, picks the split count and computes the workspace size.
- * Split rule: with T = ceil(e / 16) + 1 tiles of 16 keys for the longest attended range
- * e = min(max_ctx_len, W or unlimited), pairs = batch * Hkv and target = 2 * num_cus workgroups,
- *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, ceil(T / 8)))
- * so every chunk holds at least 8 tiles (128 keys) when the context allows it.
+ * Split rule: with T = ceil(e / 16) (+ 1 for a sliding window, whose edge may straddle a tile)
+ * tiles of 16 keys for the longest attended range
+ * e = min(max_ctx_len, W or unlimited), pairs = batch * Hkv and target = num_cus workgroups for
+ * head_dim 512 (2 * num_cus for 256),
+ *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, ceil(T / 2)))
+ * so every chunk holds at least 2 tiles (32 keys, one stage-1 loop step) when the context
+ * allows it.
  * Returns DECODE_ATTN_OK, DECODE_ATTN_ERR_NULL, _SHAPE, _UNSUPPORTED or _HIP (device query).
  */
 int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* plan);

@@ -68,7 +68,8 @@ class Plan(ctypes.Structure):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """The in-tree library, or the file named by PAGED_GQA_KV_ATTN_LIB (for A/B builds)."""
+    return os.environ.get("PAGED_GQA_KV_ATTN_LIB") or os.path.join(_HERE, _LIB_NAME)
 
 
 def load_library():

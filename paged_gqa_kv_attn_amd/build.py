@@ -45,18 +45,26 @@ def _compile(src: str, extra=()) -> str:
     return obj
 
 
-def build(extra_flags=()) -> str:
-    """Compile all sources and link the shared library; returns its path."""
+def build(extra_flags=(), out=None, obj_dir=None) -> str:
+    """Compile all sources and link the shared library; returns its path. ``extra_flags`` (e.g.
+    "-DDECODE_ATTN_STAGE1_SUB=2") and ``out``/``obj_dir`` serve A/B builds of variants."""
+    global OBJ_DIR
+    lib = out or LIB
+    saved = OBJ_DIR
+    OBJ_DIR = obj_dir or OBJ_DIR
     os.makedirs(OBJ_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    try:
+        with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            objs = list(ex.map(lambda s: _compile(s, extra_flags), SOURCES))
+    finally:
+        OBJ_DIR = saved
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [_hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH] + objs + ["-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -188,7 +188,10 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   if (p.window > 0 && e > p.window) e = p.window;
   const int64_t tiles = (e + kTile - 1) / kTile + (p.window > 0 ? 1 : 0);
   const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
-  const int64_t target = 2 * (int64_t)p.num_cus;
+  // Workgroups to aim for: one per CU for head_dim 512 (a workgroup streams one chunk with 4
+  // waves; measured on MI355X, 1 per CU is as fast as 2 and beats 1.5 or 3), two per CU for
+  // smaller heads (short per-workgroup chunks, more latency to hide).
+  const int64_t target = (p.head_dim >= 512 ? 1 : 2) * (int64_t)p.num_cus;
   int64_t splits = (target + pairs - 1) / pairs;
   int64_t cap = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
   if (cap > p.max_splits) cap = p.max_splits;

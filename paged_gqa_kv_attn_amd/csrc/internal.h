@@ -10,7 +10,7 @@ namespace decode_attn {
 constexpr uint32_t kPlanMagic = 0x44415431u;  // "DAT1"
 constexpr int kTile = 16;                     // keys per tile: the M dimension of one MFMA
 constexpr int kDefaultMaxSplits = 256;
-constexpr int kMinTilesPerSplit = 8;          // 128 keys
+constexpr int kMinTilesPerSplit = 2;          // 32 keys: one stage-1 loop step
 constexpr int kStage1Threads = 256;           // 4 wavefronts of 64 lanes
 constexpr int kStage2Threads = 256;
 

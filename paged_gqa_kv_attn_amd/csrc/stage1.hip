@@ -7,24 +7,28 @@
 // log-sum-exp, the split-KV partial buffer of vLLM learning notes "模型库与算子层 — 概念",
 // section "MLA 与 Sparse MLA（DSA）".
 //
-// Work decomposition (4 wavefronts of 64 lanes; the chunk is walked in tiles of 16 keys, a page of
-// 16 keys or a 16-key slice of a larger page; all four waves work on the same tile):
-//   * wave w owns the head-dim columns [w*D/4, (w+1)*D/4) of K, V and the output;
+// Work decomposition (NW = D / CW wavefronts of 64 lanes, each owning CW head-dim columns: CW = 128
+// for head_dim 512 and 64 for 256 by default; the chunk is walked in steps of SUB tiles of 16 keys,
+// a tile being a page of 16 keys or a 16-key slice of a larger page; all waves work on the same
+// tiles):
+//   * wave w owns the head-dim columns [CW*w, CW*w + CW) of K, V and the output;
 //   * scores: v_mfma_f32_16x16x32_bf16 with A = K tile (16 keys x 32 columns; every lane loads 16
 //     contiguous bytes of one key row straight from HBM) and B = the q group (32 columns x 16
 //     heads, heads >= G zero, kept in registers). Each wave gets the partial scores of its
-//     columns; the four partials meet in LDS (one barrier per tile) and are summed in a fixed
+//     columns; the NW partials meet in LDS (one barrier per step) and are summed in a fixed
 //     order, so every wave holds the same full scores: lane l has keys 4*(l/16)..+3 of head l%16;
 //   * softmax: keys outside [lo, n) get -inf by select (never by multiplying a mask, so NaN in
 //     unused slots cannot leak), running max and sum per head in base-2 units, hardware exp2;
 //   * P.V: v_mfma_f32_16x16x16_bf16 with A = P (16 heads x 16 keys, which is exactly the layout the
 //     score MFMA left in the lanes, rounded to bf16) and B = V (16 keys x 16 columns). V is loaded
-//     so that lane l holds 16 bytes of keys 4*(l/16)..+3 in its own column slice and is
+//     so that lane l holds CW/8 bytes of keys 4*(l/16)..+3 in its own column slice and is
 //     transposed inside the lane with byte permutes; each wave accumulates O[heads][its columns];
-//   * loads run STAGES tiles ahead in registers: the K registers of a stage are refilled right after
-//     its score MFMAs, the V registers right after its P.V MFMAs.
-// The per-head softmax state is identical in all four waves, so no merge is needed at the end:
-// each wave writes its own columns of the partial output.
+//   * loads run one step ahead in registers: the K registers are refilled for the next step right
+//     after the score MFMAs, the V registers right after the P.V MFMAs; the page ids of the step
+//     after that are fetched as a small vector (lane u holds tile u's id) one step earlier still,
+//     so no dependent block-table read sits on the critical path.
+// The per-head softmax state is identical in all waves, so no merge is needed at the end: each
+// wave writes its own columns of the partial output.
 
 #include <hip/hip_runtime.h>
 
@@ -41,11 +45,35 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = kStage1Threads / 64;
+// Build-time knobs (defaults are the values tuned on MI355X): 16-key tiles per loop step, and
+// whether K/V are read with the non-temporal hint (streamed once, no reuse worth caching).
+#ifndef DECODE_ATTN_STAGE1_SUB
+#define DECODE_ATTN_STAGE1_SUB 1
+#endif
+#ifndef DECODE_ATTN_NT_LOADS
+#define DECODE_ATTN_NT_LOADS 1
+#endif
+
+#ifndef DECODE_ATTN_COLS_PER_WAVE_512
+#define DECODE_ATTN_COLS_PER_WAVE_512 128
+#endif
+#ifndef DECODE_ATTN_COLS_PER_WAVE_256
+#define DECODE_ATTN_COLS_PER_WAVE_256 64
+#endif
+
 constexpr float kLn2 = 0.693147180559945309417f;
 
+template <typename T>
+__device__ __forceinline__ T load_stream(const uint16_t* p) {
+#if DECODE_ATTN_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+#else
+  return *reinterpret_cast<const T*>(p);
+#endif
+}
+
 // Read-only kernel inputs (block table, context lengths) are read through the constant address
-// space so uniform indices become scalar loads that do not share the vector-memory counter.
+// space so uniform indices become scalar loads.
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
 __device__ __forceinline__ int32_t load_uniform(const int32_t* p, size_t idx) {
@@ -73,25 +101,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int D>
 struct Shape {
   static_assert(D == 256 || D == 512, "head_dim");
-  static constexpr int kCols = D / kWaves;    // columns per wave
+  static constexpr int kCols = D == 512 ? DECODE_ATTN_COLS_PER_WAVE_512
+                                        : DECODE_ATTN_COLS_PER_WAVE_256;  // columns per wave
+  static_assert(kCols == 64 || kCols == 128, "columns per wave");
+  static constexpr int kWaves = D / kCols;
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kKSteps = kCols / 32;  // score MFMAs per tile per wave
-  static constexpr int kVE = kCols / 16;      // columns per lane in a V row (8 or 4)
-  static constexpr int kVDwords = kVE / 2;    // dwords per lane per V row
+  static constexpr int kVE = kCols / 16;      // columns per lane in a V row (4 or 8)
+  static constexpr int kVDwords = kVE / 2;
+  using VRow = typename std::conditional<kVDwords == 4, u32x4, u32x2>::type;
 };
-
-template <int D>
-using VRow = typename std::conditional<Shape<D>::kVDwords == 4, u32x4, u32x2>::type;
 
 // One step's worth of this wave's slice of K and V: SUB tiles of 16 keys.
 template <int D, int SUB>
 struct StepRegs {
   bf16x8 k[SUB][Shape<D>::kKSteps];
-  VRow<D> v[SUB][4];  // tile u, keys 4*(lane/16)+i, i = 0..3
+  typename Shape<D>::VRow v[SUB][4];  // tile u, keys 4*(lane/16)+i, i = 0..3
 };
 
 template <int D, int G, int SUB>
-__global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1Args a) {
+__global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1Args a) {
   using Sh = Shape<D>;
+  constexpr int kWaves = Sh::kWaves;
   constexpr int kKSteps = Sh::kKSteps;
   constexpr int kVE = Sh::kVE;
 
@@ -106,7 +137,9 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
   const int col = lane & 15;  // column (scores: head; P.V: column block)
   const int S = a.page_size;
   const int ns = a.num_splits;
-  const int c0 = wave * Sh::kCols;  // first head-dim column of this wave
+  constexpr int kCols = Sh::kCols;
+  using VRow = typename Sh::VRow;
+  const int c0 = wave * kCols;  // first head-dim column of this wave
   const size_t row0 = (size_t)b * a.num_q_heads + (size_t)kvh * G;
 
   // Key range of this sequence and the tiles of this split.
@@ -120,12 +153,12 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
   const int t_begin = tile_lo + (int)(((int64_t)split * T) / ns);
   const int t_end = tile_lo + (int)(((int64_t)(split + 1) * T) / ns);
   const int tiles_per_page = S / kTile;
-  const size_t table_row = (size_t)b * a.max_pages_per_seq;
+  const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
 
   if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
-    for (int idx = lane; idx < G * Sh::kCols; idx += 64) {
-      const int h = idx / Sh::kCols;
-      a.o_part[((row0 + h) * ns + split) * D + c0 + (idx - h * Sh::kCols)] = 0.f;
+    for (int idx = lane; idx < G * kCols; idx += 64) {
+      const int h = idx / kCols;
+      a.o_part[((row0 + h) * ns + split) * D + c0 + (idx - h * kCols)] = 0.f;
     }
     if (wave == 0 && lane < G) a.lse_part[(row0 + lane) * ns + split] = -INFINITY;
     return;
@@ -151,34 +184,42 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
   const int k_off = col * D + c0 + 8 * grp;
   const int v_off = (4 * grp) * D + c0 + kVE * col;
 
-  // Tile -> element offset of its first key in the pools. Tiles past the split re-read its last
-  // tile (an L2 hit; they are masked) so every load is unconditional and the compiler can count
-  // outstanding loads exactly. Invalid page ids are never dereferenced: page 0 is read instead
-  // and the tile is masked.
-  auto tile_base = [&](int ti, bool& ok) -> size_t {
-    const int tc = ti < t_end ? ti : t_last;
-    const int pc = tc / tiles_per_page;
-    int phys = load_uniform(a.block_table, table_row + pc);
-    ok = ti < t_end && (unsigned)phys < (unsigned)a.num_pages;
-    phys = (unsigned)phys < (unsigned)a.num_pages ? phys : 0;
-    return (((size_t)phys * a.num_kv_heads + kvh) * S + (tc - pc * tiles_per_page) * kTile) * D;
+  // Tiles past the split re-read its last tile (an L2 hit; they are masked) so every load is
+  // unconditional and the compiler can count outstanding loads exactly. Invalid page ids are
+  // never dereferenced: page 0 is read instead and the tile is masked.
+  auto clamp_tile = [&](int ti) { return ti < t_end ? ti : t_last; };
+  auto tile_base = [&](int ti, int phys, bool& ok) -> size_t {
+    const int tc = clamp_tile(ti);
+    const bool page_ok = (unsigned)phys < (unsigned)a.num_pages;
+    ok = ti < t_end && page_ok;
+    const int pg = page_ok ? phys : 0;
+    const int within = tc - (tc / tiles_per_page) * tiles_per_page;
+    return (((size_t)pg * a.num_kv_heads + kvh) * S + within * kTile) * D;
+  };
+  // Page ids of tiles t .. t+SUB-1 as a vector: lane u holds tile (t + u % SUB)'s id.
+  auto load_page_ids = [&](int t) -> int32_t {
+    const int tc = clamp_tile(t + lane % SUB);
+    return table_row[tc / tiles_per_page];
   };
 
   StepRegs<D, SUB> r;
   size_t base[SUB];
   bool ok[SUB];
 #pragma unroll
-  for (int u = 0; u < SUB; ++u) base[u] = tile_base(t_begin + u, ok[u]);
+  for (int u = 0; u < SUB; ++u) {
+    const int tc = clamp_tile(t_begin + u);
+    base[u] = tile_base(t_begin + u, load_uniform(table_row, tc / tiles_per_page), ok[u]);
+  }
+  int32_t pid_next = load_page_ids(t_begin + SUB);
 #pragma unroll
   for (int u = 0; u < SUB; ++u)
 #pragma unroll
     for (int j = 0; j < kKSteps; ++j)
-      r.k[u][j] = *reinterpret_cast<const bf16x8*>(a.k_pool + base[u] + k_off + 32 * j);
+      r.k[u][j] = load_stream<bf16x8>(a.k_pool + base[u] + k_off + 32 * j);
 #pragma unroll
   for (int u = 0; u < SUB; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r.v[u][i] = *reinterpret_cast<const VRow<D>*>(a.v_pool + base[u] + v_off + i * D);
+    for (int i = 0; i < 4; ++i) r.v[u][i] = load_stream<VRow>(a.v_pool + base[u] + v_off + i * D);
   // A fence the loop latch does not have: otherwise the identical trailing V loads of this
   // prologue and of the loop body get merged into the loop header, which would turn the V
   // prefetch into a load at the top of every step.
@@ -186,7 +227,7 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
 
   float m_run = -INFINITY;  // running max (base-2 units) of head `col`
   float l_run = 0.f;        // running sum of exp2(s - m_run) of head `col`
-  f32x4 acc[kVE];           // O[head 4*grp + r][column c0 + kVE*col + e] = acc[e][r]
+  f32x4 acc[kVE];           // O[head 4*grp + i][column c0 + kVE*col + e] = acc[e][i]
 #pragma unroll
   for (int e = 0; e < kVE; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -205,19 +246,21 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
       score_lds[buf][u][wave][lane] = p0 + p1;
     }
 
-    // Next step's K into the registers just consumed. The scheduling barriers keep loads in
-    // program order (K of step i+1 before V of step i+1), which the wait counts rely on.
+    // Next step's K into the registers just consumed, then the page ids of the step after. The
+    // scheduling barriers keep loads in program order, which the wait counts rely on.
     __builtin_amdgcn_sched_barrier(0);
     const int tn = t0 + SUB;
     bool ok_n[SUB];
     size_t base_n[SUB];
 #pragma unroll
-    for (int u = 0; u < SUB; ++u) base_n[u] = tile_base(tn + u, ok_n[u]);
+    for (int u = 0; u < SUB; ++u)
+      base_n[u] = tile_base(tn + u, __builtin_amdgcn_readlane(pid_next, u), ok_n[u]);
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
       for (int j = 0; j < kKSteps; ++j)
-        r.k[u][j] = *reinterpret_cast<const bf16x8*>(a.k_pool + base_n[u] + k_off + 32 * j);
+        r.k[u][j] = load_stream<bf16x8>(a.k_pool + base_n[u] + k_off + 32 * j);
+    const int32_t pid_after = load_page_ids(tn + SUB);
     __builtin_amdgcn_sched_barrier(0);
 
     lds_barrier();
@@ -270,7 +313,7 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
     l_run = l_run * alpha + ps;
     m_run = m_new;
 
-    // Rescale the accumulator rows (heads 4*grp + r) when some running max moved.
+    // Rescale the accumulator rows (heads 4*grp + i) when some running max moved.
     if (__any(alpha != 1.f)) {
       float al[4];
 #pragma unroll
@@ -284,7 +327,7 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
     // P.V, one tile at a time.
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
-      VRow<D> vr[4];
+      VRow vr[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) vr[i] = r.v[u][i];
       if (!full) {  // masked keys: V := 0 (their p is 0, but 0 * NaN would not be)
@@ -316,9 +359,10 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        r.v[u][i] = *reinterpret_cast<const VRow<D>*>(a.v_pool + base_n[u] + v_off + i * D);
+        r.v[u][i] = load_stream<VRow>(a.v_pool + base_n[u] + v_off + i * D);
 #pragma unroll
     for (int u = 0; u < SUB; ++u) ok[u] = ok_n[u];
+    pid_next = pid_after;
   }
 
   // Normalise and write this wave's columns of the partial output; lane holds heads 4*grp + i.
@@ -329,14 +373,11 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
     if (h < G) {
       float* dst = a.o_part + ((row0 + h) * ns + split) * D + c0 + kVE * col;
-      if constexpr (kVE == 8) {
-        const f32x4 lo4 = {acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
-        const f32x4 hi4 = {acc[4][i] * inv, acc[5][i] * inv, acc[6][i] * inv, acc[7][i] * inv};
-        reinterpret_cast<f32x4*>(dst)[0] = lo4;
-        reinterpret_cast<f32x4*>(dst)[1] = hi4;
-      } else {
-        const f32x4 v4 = {acc[0][i] * inv, acc[1][i] * inv, acc[2][i] * inv, acc[3][i] * inv};
-        reinterpret_cast<f32x4*>(dst)[0] = v4;
+#pragma unroll
+      for (int e4 = 0; e4 < kVE; e4 += 4) {
+        const f32x4 v4 = {acc[e4][i] * inv, acc[e4 + 1][i] * inv, acc[e4 + 2][i] * inv,
+                          acc[e4 + 3][i] * inv};
+        *reinterpret_cast<f32x4*>(dst + e4) = v4;
       }
     }
   }
@@ -348,12 +389,12 @@ __global__ __launch_bounds__(kStage1Threads, 2) void stage1_kernel(const Stage1A
 
 template <int D, int G>
 hipError_t launch(const Stage1Args& args, int batch, hipStream_t stream) {
-  constexpr int kSub = 4;  // tiles of 16 keys per loop step
+  constexpr int kSub = DECODE_ATTN_STAGE1_SUB;
   dim3 grid(args.num_splits, args.num_kv_heads, batch);
-  dim3 block(kStage1Threads);
+  dim3 block(Shape<D>::kThreads);
   void* kargs[] = {const_cast<Stage1Args*>(&args)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub>), grid,
-                         block, kargs, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub>), grid, block,
+                         kargs, 0, stream);
 }
 
 template <int D>

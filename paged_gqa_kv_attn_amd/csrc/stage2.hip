@@ -7,9 +7,12 @@
 //     lse = M + ln(sum_s w_s)
 // (an empty chunk has lse = -inf and weight 0; all empty gives out = 0, lse = -inf).
 //
-// One workgroup per (64-wide slice of d, query head, sequence): lane l owns d = slice*64 + l, so
-// every partial row is read with one coalesced 256-byte access per wave; the 4 waves take splits
-// w, w+4, ... and are combined in LDS in a fixed order.
+// One pass: one workgroup per (64-wide slice of d, query head, sequence), 256 threads = 16 split
+// groups of 16 threads; a thread owns 4 consecutive d and walks splits g, g+16, ... in batches of
+// kBatch whose loads (partial rows and their lse) are all issued before any is used. Each thread
+// keeps a running max, weight sum and weighted sum (rescaled when the max grows), so no separate
+// pass over the lse values is needed. The 16 group states are merged in LDS in a fixed order
+// (deterministic).
 
 #include <hip/hip_runtime.h>
 
@@ -18,63 +21,90 @@
 namespace decode_attn {
 namespace {
 
-constexpr int kWaves2 = kStage2Threads / 64;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kGroups = 16;                              // split groups per workgroup
+constexpr int kGroupThreads = kStage2Threads / kGroups;  // 16 threads x 4 d = 64 d
+constexpr int kBatch = 8;                                // splits per thread per round of loads
 constexpr float kLog2e = 1.442695040888963407360f;
 constexpr float kLn2f = 0.693147180559945309417f;
 
 __global__ __launch_bounds__(kStage2Threads) void stage2_kernel(const Stage2Args a) {
-  __shared__ float red_lds[kWaves2];
-  __shared__ float acc_lds[kWaves2][64];
-  __shared__ float wsum_lds[kWaves2];
+  __shared__ f32x4 acc_lds[kGroups][kGroupThreads];
+  __shared__ float m_lds[kGroups];
+  __shared__ float w_lds[kGroups];
 
   const int slice = blockIdx.x;
   const int h = blockIdx.y;
   const int b = blockIdx.z;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int g = tid / kGroupThreads;
+  const int t = tid % kGroupThreads;
   const int ns = a.num_splits;
   const int D = a.head_dim;
   const size_t row = (size_t)b * a.num_q_heads + h;
   const float* lse = a.lse_part + row * ns;
+  const int d = slice * 64 + 4 * t;
+  const f32x4* o = reinterpret_cast<const f32x4*>(a.o_part + row * (size_t)ns * D + d);
+  const size_t stride = (size_t)D / 4;  // f32x4 per partial row
 
-  // M = max over splits.
-  float m = -INFINITY;
-  for (int s = threadIdx.x; s < ns; s += kStage2Threads) m = fmaxf(m, lse[s]);
+  // Running state in base-2 units: max m, weight sum w, weighted sum acc (all relative to m).
+  float m = -INFINITY, wsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = g; s0 < ns; s0 += kGroups * kBatch) {
+    float l[kBatch];
+    f32x4 v[kBatch];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) red_lds[wave] = m;
-  __syncthreads();
-  float M = red_lds[0];
+    for (int k = 0; k < kBatch; ++k) {
+      const int s = s0 + k * kGroups;
+      const int sc = s < ns ? s : s0;  // in-bounds; out-of-range entries get weight 0 below
+      l[k] = lse[sc];
+      v[k] = o[(size_t)sc * stride];
+    }
+    float bm = m;
 #pragma unroll
-  for (int w = 1; w < kWaves2; ++w) M = fmaxf(M, red_lds[w]);
-
-  // Weighted sum over this wave's splits.
-  const int d = slice * 64 + lane;
-  const float* o = a.o_part + row * (size_t)ns * D + d;
-  float acc = 0.f, wsum = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 4
-    for (int s = wave; s < ns; s += kWaves2) {
-      const float l = lse[s];
-      const float w = (l == -INFINITY) ? 0.f : exp2f((l - M) * kLog2e);
-      acc = fmaf(w, o[(size_t)s * D], acc);
-      wsum += w;
+    for (int k = 0; k < kBatch; ++k) {
+      l[k] = (s0 + k * kGroups < ns) ? l[k] * kLog2e : -INFINITY;
+      bm = fmaxf(bm, l[k]);
+    }
+    if (bm != -INFINITY) {
+      const float r = exp2f(m - bm);  // m == -inf gives 0
+      wsum *= r;
+      acc *= r;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float w = exp2f(l[k] - bm);  // -inf gives 0
+        wsum += w;
+        acc += w * v[k];
+      }
+      m = bm;
     }
   }
-  acc_lds[wave][lane] = acc;
-  if (lane == 0) wsum_lds[wave] = wsum;
+  acc_lds[g][t] = acc;
+  if (t == 0) {
+    m_lds[g] = m;
+    w_lds[g] = wsum;
+  }
   __syncthreads();
 
-  if (wave == 0) {
-    float tot = 0.f, W = 0.f;
+  if (g == 0) {
+    float M = m_lds[0];
 #pragma unroll
-    for (int w = 0; w < kWaves2; ++w) {
-      tot += acc_lds[w][lane];
-      W += wsum_lds[w];
+    for (int k = 1; k < kGroups; ++k) M = fmaxf(M, m_lds[k]);
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};
+    float W = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < kGroups; ++k) {
+        const float r = exp2f(m_lds[k] - M);
+        tot += r * acc_lds[k][t];
+        W += r * w_lds[k];
+      }
     }
-    a.out[row * D + d] = (M == -INFINITY) ? 0.f : tot / W;
-    if (a.lse_out != nullptr && slice == 0 && lane == 0)
-      a.lse_out[row] = (M == -INFINITY) ? -INFINITY : M + __log2f(W) * kLn2f;
+    const float inv = (M == -INFINITY) ? 0.f : 1.f / W;
+    *reinterpret_cast<f32x4*>(a.out + row * D + d) = tot * inv;
+    if (a.lse_out != nullptr && slice == 0 && t == 0)
+      a.lse_out[row] = (M == -INFINITY) ? -INFINITY : (M + __log2f(W)) * kLn2f;
   }
 }
 

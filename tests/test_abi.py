@@ -65,12 +65,13 @@ def expected_workspace(B, Hq, ns, D):
 
 
 @pytest.mark.parametrize("kw,splits", [
-    (dict(), 64),                                                     # 4 x 33792 global
-    (dict(batch=1, max_pages_per_seq=8256, num_pages=16384, max_ctx_len=132096), 256),
-    (dict(batch=2, max_pages_per_seq=4160, num_pages=16384, max_ctx_len=66560), 128),
-    (dict(batch=8, max_pages_per_seq=80, max_ctx_len=1280), 10),      # capped: >= 8 tiles/split
-    (dict(num_kv_heads=8, head_dim=256, window=1024), 9),             # 65 tiles -> ceil(65/8)
-    (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024), 8),
+    (dict(), 32),                                                     # 4 x 33792 global
+    (dict(batch=1, max_pages_per_seq=8256, num_pages=16384, max_ctx_len=132096), 128),
+    (dict(batch=2, max_pages_per_seq=4160, num_pages=16384, max_ctx_len=66560), 64),
+    (dict(batch=8, max_pages_per_seq=80, max_ctx_len=1280), 16),      # 16 pairs
+    (dict(num_kv_heads=8, head_dim=256, window=1024), 16),            # 65 tiles, 32 pairs
+    (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024), 32),
+    (dict(batch=1, max_pages_per_seq=4, max_ctx_len=64), 2),          # capped: >= 2 tiles/split
 ])
 def test_plan_split_counts(kw, splits):
     p = plan(**kw)
@@ -84,10 +85,13 @@ def test_plan_split_counts(kw, splits):
 
 
 def test_plan_long_context_split_counts_meet_chunk_rules():
-    # the 32K+ global layers get 16-64 chunks per sequence; the 64K/128K ones >= 128
+    # 32K global layer, batch 4: 16-64 chunks per sequence; 128K batch 1: >= 128 chunks; 64K batch
+    # 2: >= 128 chunks in the launch (64 per sequence)
     assert 16 <= plan().num_splits <= 64
     assert plan(batch=1, max_pages_per_seq=8256, num_pages=16384,
                 max_ctx_len=132096).num_splits >= 128
+    assert 2 * plan(batch=2, max_pages_per_seq=4160, num_pages=16384,
+                    max_ctx_len=66560).num_splits >= 128
 
 
 def test_plan_force_and_cap():
