@@ -171,6 +171,23 @@ def main() -> int:
     t1 = time.perf_counter()
 
     ms_per_step = (t1 - t0) * 1e3 / K
+
+    # Per-layer breakdown, after (outside) the timed region: events around each layer call.
+    detail = {}
+    for L in layers:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(min(K, 20))]
+        for i, (ea, eb) in enumerate(evs):
+            ea.record(stream)
+            run_layer(L, i % R)
+            eb.record(stream)
+        torch.cuda.synchronize()
+        us = sorted(1e3 * ea.elapsed_time(eb) for ea, eb in evs)
+        med = us[len(us) // 2]
+        detail[L["kind"]] = {"us_per_call_median": round(med, 2),
+                             "GB_per_s": round(L["bytes"] / (med * 1e-6) / 1e9, 1),
+                             "pct_of_hbm_peak": round(100 * L["bytes"] / (med * 1e-6) / 1e9 /
+                                                      PEAK_HBM_GBS, 2)}
     step_bytes = sum(L["bytes"] for L in layers)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     s1_ms = [a.elapsed_time(b) for a, b in ev]
@@ -226,6 +243,7 @@ def main() -> int:
             "algorithmic_bytes_per_launch": s1_bytes,
         },
         "cpu_baseline": None,
+        "layers_detail": detail,
     }
 
     if not args.no_cpu_baseline:
