@@ -68,6 +68,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--k-eq-v", action="store_true",
+                    help="layers whose values are their keys: one pool passed as both K and V")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -111,13 +113,17 @@ def main() -> int:
         d = inp.dims
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
             torch.bfloat16)
-        k0, v0 = bf(inp.k_pool), bf(inp.v_pool)
+        if args.k_eq_v:
+            inp.v_pool = inp.k_pool
+        k0 = bf(inp.k_pool)
+        v0 = k0 if args.k_eq_v else bf(inp.v_pool)
         ks, vs = [k0], [v0]
         for _ in range(1, max(1, args.copies)):
             ks.append(k0.clone())
-            vs.append(v0.clone())
+            vs.append(ks[-1] if args.k_eq_v else v0.clone())
         plan = pda.decode_attn_plan(d["B"], d["Hq"], d["Hkv"], d["D"], d["S"], d["M"], d["P"],
-                                    max_ctx_len=int(inp.ctx_lens.max()), window=inp.window)
+                                    max_ctx_len=int(inp.ctx_lens.max()), window=inp.window,
+                                    values_are_keys=args.k_eq_v)
         spec = wl.layers[kind]
         layers.append(dict(
             kind=kind, inp=inp, dims=d, plan=plan, q=bf(inp.q), k=ks, v=vs,
@@ -127,7 +133,8 @@ def main() -> int:
             lse=torch.empty((d["B"], d["Hq"]), device=dev),
             ws=torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev),
             bytes=wl_mod.algorithmic_bytes(inp.ctx_lens, spec.num_q_heads, spec.num_kv_heads,
-                                           spec.head_dim, wl.page_size, spec.window),
+                                           spec.head_dim, wl.page_size, spec.window,
+                                           k_eq_v=args.k_eq_v),
             flops=wl_mod.algorithmic_flops(inp.ctx_lens, spec.num_q_heads, spec.head_dim,
                                            spec.window)))
         del inp.k_pool, inp.v_pool  # host copies are regenerated for the CPU leg if needed
@@ -228,6 +235,7 @@ def main() -> int:
                                        algorithmic_bytes=L["bytes"]) for L in layers},
             "step_algorithmic_bytes": step_bytes,
             "kv_pool_copies_rotated": R,
+            "k_eq_v": bool(args.k_eq_v),
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -250,6 +258,9 @@ def main() -> int:
         import oracle
         oracle.build(force=False)
         host = [wl_mod.make_workload_layer(args.workload, L["kind"]) for L in layers]
+        if args.k_eq_v:
+            for h in host:
+                h.v_pool = h.k_pool
         gpu_out = [(L["out"].cpu().double().numpy(), L["lse"].cpu().double().numpy())
                    for L in layers]
         reps, t_cpu, refs = 0, 0.0, None

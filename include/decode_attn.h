@@ -32,7 +32,10 @@
  * Layouts (all row-major, contiguous, device memory):
  *     q            [B, Hq, D]             bf16
  *     k_pool       [P, Hkv, S, D]         bf16   one (page, kv head) block is S*D contiguous values
- *     v_pool       [P, Hkv, S, D]         bf16
+ *     v_pool       [P, Hkv, S, D]         bf16   the same buffer as k_pool for layers whose values
+ *                                                are their keys (K = V, Sparse-vLLM PR #27, section
+ *                                                "Gemma 4 文本推理"): plan them with
+ *                                                values_are_keys = 1 and pass one pool twice
  *     block_table  [B, max_pages_per_seq] int32  physical page ids; entries of pages holding no key
  *                                                in [lo, n) are never read and may hold anything
  *     ctx_lens     [B]                    int32
@@ -92,6 +95,8 @@ typedef struct {
   int32_t num_cus;           /* compute units to plan for; 0 = query the current HIP device */
   int32_t max_splits;        /* cap on num_splits; 0 = library default (256) */
   int32_t force_splits;      /* 0 = the planner chooses; > 0 = use exactly this many (<= 1024) */
+  int32_t values_are_keys;   /* 1: the layer's values are its keys and calls pass one pool as both
+                                k_pool and v_pool (each tile is then read once); 0: separate pools */
 } decode_attn_problem;
 
 /* A plan: plain data, copy it freely; there is nothing to free. */
@@ -113,7 +118,7 @@ typedef struct {
  * Split rule: with T = ceil(e / 16) (+ 1 for a sliding window, whose edge may straddle a tile)
  * tiles of 16 keys for the longest attended range
  * e = min(max_ctx_len, W or unlimited), pairs = batch * Hkv and target = num_cus workgroups for
- * head_dim 512 (2 * num_cus for 256),
+ * head_dim 512 with separate pools (2 * num_cus for head_dim 256 or when values are keys),
  *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, ceil(T / 2)))
  * so every chunk holds at least 2 tiles (32 keys, one stage-1 loop step) when the context
  * allows it.
@@ -125,7 +130,9 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
  * decode_attn_global — attention of a global layer (plan->problem.window == 0): stage 1 then
  * stage 2 on `stream`. `batch` (0 <= batch <= plan->problem.batch) sequences are computed; batch 0
  * returns DECODE_ATTN_OK without launching. `scale` multiplies q.k (1/sqrt(D) for Gemma-style
- * layers). lse_out may be NULL. workspace must hold plan->workspace_bytes.
+ * layers). lse_out may be NULL. workspace must hold plan->workspace_bytes. A plan made with
+ * values_are_keys = 1 requires v_pool == k_pool (else DECODE_ATTN_ERR_SHAPE); the same pool passed
+ * twice under a plan without it is computed correctly, with the other split count.
  */
 int decode_attn_global(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
                        const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
@@ -167,6 +174,21 @@ int decode_attn_stage1(const decode_attn_plan_t* plan, const void* q, const void
  */
 int decode_attn_stage2(const decode_attn_plan_t* plan, int32_t batch, const void* workspace,
                        uint64_t workspace_bytes, float* out, float* lse_out, void* stream);
+
+/*
+ * decode_attn_append_kv — write each sequence's newest key and value into the paged pools before
+ * attention reads them (the cache-manager write of Sparse-vLLM PR #27, section
+ * "Gemma 4 文本推理"; ctx_lens counts the new token). For b < batch with n = ctx_lens[b] >= 1,
+ * token t = n - 1 goes to page block_table[b, t / S], slot t % S, for every KV head g:
+ *     k_pool[page, g, t % S, :] = k_new[b, g, :]    and the same for V.
+ * k_new, v_new: [B, Hkv, D] bf16, 16-byte aligned. v_pool may equal k_pool (layers whose values
+ * are their keys): then only k_new is written and v_new may be NULL. A position outside the
+ * table row or a page id outside [0, P) is skipped (nothing written for that sequence). Any plan
+ * of the layer can be used (only its shape is read). Bitwise copy; asynchronous on `stream`.
+ */
+int decode_attn_append_kv(const decode_attn_plan_t* plan, const void* k_new, const void* v_new,
+                          void* k_pool, void* v_pool, const int32_t* block_table,
+                          const int32_t* ctx_lens, int32_t batch, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_str(int status);

@@ -57,6 +57,8 @@ def _load():
     lib.oracle_lse_merge.restype = ctypes.c_int
     lib.oracle_key_range.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.oracle_key_range.restype = None
+    lib.oracle_append_kv.argtypes = [i32] * 6 + [vp] * 6
+    lib.oracle_append_kv.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -142,6 +144,27 @@ def lse_merge(o_parts, lses):
     if rc != 0:
         raise ValueError("oracle_lse_merge failed with code %d" % rc)
     return out, lse
+
+
+def append_kv(k_new, v_new, k_pool, v_pool, block_table, ctx_lens):
+    """Write each sequence's newest token (position ctx_lens[b] - 1) into the pools, in place.
+    ``v_pool is k_pool`` writes K only (layers whose values are their keys)."""
+    lib = _load()
+    same = v_pool is k_pool
+    for a in (k_new, k_pool) + (() if same else (v_new, v_pool)):
+        if a.dtype != np.uint16 or not a.flags.c_contiguous:
+            raise TypeError("bf16 bit patterns (uint16), C-contiguous, expected")
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx_lens = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    B, Hkv, D = k_new.shape
+    P, Hkv2, S, D2 = k_pool.shape
+    if Hkv2 != Hkv or D2 != D or block_table.shape[0] != B:
+        raise ValueError("inconsistent shapes")
+    rc = lib.oracle_append_kv(B, Hkv, D, S, block_table.shape[1], P, _ptr(k_new),
+                              _ptr(k_new if same else v_new), _ptr(k_pool),
+                              _ptr(k_pool if same else v_pool), _ptr(block_table), _ptr(ctx_lens))
+    if rc != 0:
+        raise ValueError("oracle_append_kv failed with code %d" % rc)
 
 
 def max_threads() -> int:

@@ -202,6 +202,38 @@ int oracle_lse_merge(int32_t rows, int32_t splits, int32_t D, const double* o_pa
   return ORACLE_OK;
 }
 
+/*
+ * Paged KV append: the newest token of each sequence (position n - 1, n = ctx_lens[b]; the
+ * context length counts it) is written into its slot, page block_table[b, (n-1) / S], slot
+ * (n-1) % S, for every KV head g: pool[page, g, slot, :] = new[b, g, :]. Sequences with n <= 0
+ * are left alone. When v_pool == k_pool (layers whose values are their keys) only K is written.
+ * Returns ORACLE_BAD_PAGE if a slot lies outside the table row or the pool (nothing written for it).
+ */
+int oracle_append_kv(int32_t B, int32_t Hkv, int32_t D, int32_t S, int32_t max_pages_per_seq,
+                     int32_t num_pages, const uint16_t* k_new, const uint16_t* v_new,
+                     uint16_t* k_pool, uint16_t* v_pool, const int32_t* block_table,
+                     const int32_t* ctx_lens) {
+  if (B < 0 || Hkv <= 0 || D <= 0 || S <= 0) return ORACLE_BAD_ARG;
+  int status = ORACLE_OK;
+  for (int32_t b = 0; b < B; ++b) {
+    const int32_t n = ctx_lens[b];
+    if (n <= 0) continue;
+    const int32_t t = n - 1;
+    const int32_t col = t / S;
+    if (col >= max_pages_per_seq) { status = ORACLE_BAD_PAGE; continue; }
+    const int32_t page = block_table[(int64_t)b * max_pages_per_seq + col];
+    if (page < 0 || page >= num_pages) { status = ORACLE_BAD_PAGE; continue; }
+    for (int32_t g = 0; g < Hkv; ++g) {
+      const int64_t dst = (((int64_t)page * Hkv + g) * S + (t % S)) * D;
+      const int64_t src = ((int64_t)b * Hkv + g) * D;
+      for (int32_t d = 0; d < D; ++d) k_pool[dst + d] = k_new[src + d];
+      if (v_pool != k_pool)
+        for (int32_t d = 0; d < D; ++d) v_pool[dst + d] = v_new[src + d];
+    }
+  }
+  return status;
+}
+
 /* Threads the OpenMP runtime would use (reported by the CPU baseline). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

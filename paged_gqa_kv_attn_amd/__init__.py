@@ -8,6 +8,7 @@ and a missing or unloadable library raises an error: there is no fallback.
 from .binding import (  # noqa: F401
     DecodeAttnError,
     Plan,
+    decode_attn_append_kv,
     decode_attn_global,
     decode_attn_plan,
     decode_attn_sliding,

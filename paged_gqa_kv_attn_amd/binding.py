@@ -42,7 +42,8 @@ class DecodeAttnError(RuntimeError):
 class Problem(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "max_pages_per_seq",
-        "num_pages", "max_ctx_len", "window", "num_cus", "max_splits", "force_splits")]
+        "num_pages", "max_ctx_len", "window", "num_cus", "max_splits", "force_splits",
+        "values_are_keys")]
 
 
 class Plan(ctypes.Structure):
@@ -80,7 +81,13 @@ def load_library():
     path = library_path()
     if not os.path.exists(path):
         raise RuntimeError("%s is not built; run __graft_entry__.build() first" % path)
+    # PyTorch ships its own HIP runtime. Loading torch first makes the dynamic linker resolve this
+    # library's libamdhip64.so.7 to that same runtime, so torch's streams, events and device memory
+    # and this library's launches belong to one runtime (loading this library first would map a
+    # second HIP/HSA runtime into the process).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
+    _check_single_runtime()
     vp, i32, u64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_float
     pplan = ctypes.POINTER(Plan)
     lib.decode_attn_plan.argtypes = [ctypes.POINTER(Problem), pplan]
@@ -89,8 +96,9 @@ def load_library():
                                         vp]
     lib.decode_attn_stage1.argtypes = [pplan, vp, vp, vp, vp, vp, i32, f32, vp, u64, vp]
     lib.decode_attn_stage2.argtypes = [pplan, i32, vp, u64, vp, vp, vp]
+    lib.decode_attn_append_kv.argtypes = [pplan, vp, vp, vp, vp, vp, vp, i32, vp]
     for fn in ("decode_attn_plan", "decode_attn_global", "decode_attn_sliding",
-               "decode_attn_stage1", "decode_attn_stage2"):
+               "decode_attn_stage1", "decode_attn_stage2", "decode_attn_append_kv"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.decode_attn_status_str.argtypes = [ctypes.c_int]
     lib.decode_attn_status_str.restype = ctypes.c_char_p
@@ -98,6 +106,18 @@ def load_library():
     lib.decode_attn_version.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+def _check_single_runtime() -> None:
+    """Raise if more than one HIP runtime is mapped into this process."""
+    try:
+        with open("/proc/self/maps") as f:
+            libs = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return
+    if len(libs) > 1:
+        raise RuntimeError("two HIP runtimes are loaded (%s); import torch before loading %s"
+                           % (sorted(libs), _LIB_NAME))
 
 
 def _check(status: int, where: str) -> None:
@@ -140,12 +160,12 @@ def _stream_handle(stream) -> Optional[int]:
 
 def decode_attn_plan(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq,
                      num_pages, max_ctx_len=0, window=0, num_cus=0, max_splits=0,
-                     force_splits=0) -> Plan:
+                     force_splits=0, values_are_keys=False) -> Plan:
     """Host-only planning (see decode_attn_plan in the header). Returns the plan struct."""
     lib = load_library()
     prob = Problem(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
                    int(max_pages_per_seq), int(num_pages), int(max_ctx_len), int(window),
-                   int(num_cus), int(max_splits), int(force_splits))
+                   int(num_cus), int(max_splits), int(force_splits), int(bool(values_are_keys)))
     plan = Plan()
     _check(lib.decode_attn_plan(ctypes.byref(prob), ctypes.byref(plan)), "decode_attn_plan")
     return plan
@@ -215,6 +235,18 @@ def decode_attn_stage2(plan: Plan, batch, workspace, out, lse_out=None, workspac
     _check(lib.decode_attn_stage2(
         ctypes.byref(plan), int(batch), ws, wsb, _dev_ptr(out, "out", _f32()),
         _dev_ptr(lse_out, "lse_out", _f32()), _stream_handle(stream)), "decode_attn_stage2")
+
+
+def decode_attn_append_kv(plan: Plan, k_new, v_new, k_pool, v_pool, block_table, ctx_lens, batch,
+                          stream=None) -> None:
+    """Write each sequence's newest K/V (position ctx_lens[b] - 1) into the pools. Passing the
+    same tensor as k_pool and v_pool writes K only (v_new may be None)."""
+    lib = load_library()
+    _check(lib.decode_attn_append_kv(
+        ctypes.byref(plan), _dev_ptr(k_new, "k_new", _bf16()), _dev_ptr(v_new, "v_new", _bf16()),
+        _dev_ptr(k_pool, "k_pool", _bf16()), _dev_ptr(v_pool, "v_pool", _bf16()),
+        _dev_ptr(block_table, "block_table", _i32()), _dev_ptr(ctx_lens, "ctx_lens", _i32()),
+        int(batch), _stream_handle(stream)), "decode_attn_append_kv")
 
 
 def decode_attn_status_str(status: int) -> str:

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdecode_attn.so")
-SOURCES = ["decode_attn.cpp", "stage1.hip", "stage2.hip"]
+SOURCES = ["decode_attn.cpp", "stage1.hip", "stage2.hip", "append.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU instructions are kept out of the generated code.

@@ -44,10 +44,27 @@ struct Stage2Args {
   int32_t num_splits;
 };
 
-// Launchers (stage1.hip / stage2.hip). They return the launch status and touch nothing else.
+// Kernel arguments of the paged KV append (one workgroup per (sequence, KV head)).
+struct AppendArgs {
+  const uint16_t* k_new;        // [B, Hkv, D] bf16
+  const uint16_t* v_new;        // [B, Hkv, D] bf16 (unused when v_pool == k_pool)
+  uint16_t* k_pool;             // [P, Hkv, S, D] bf16
+  uint16_t* v_pool;             // [P, Hkv, S, D] bf16, may equal k_pool
+  const int32_t* block_table;   // [B, max_pages_per_seq]
+  const int32_t* ctx_lens;      // [B]
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+};
+
+// Launchers (stage1.hip / stage2.hip / append.hip). They return the launch status only. Stage 1
+// picks its single-read variant when k_pool == v_pool.
 hipError_t launch_stage1(const Stage1Args& args, int head_dim, int group_size, int batch,
                          hipStream_t stream);
 hipError_t launch_stage2(const Stage2Args& args, int batch, hipStream_t stream);
+hipError_t launch_append(const AppendArgs& args, int batch, hipStream_t stream);
 
 // True when a stage-1 kernel is compiled for (head_dim, group_size).
 bool stage1_supported(int head_dim, int group_size);

@@ -119,7 +119,10 @@ struct StepRegs {
   typename Shape<D>::VRow v[SUB][4];  // tile u, keys 4*(lane/16)+i, i = 0..3
 };
 
-template <int D, int G, int SUB>
+// SHARED: the pools are one buffer (layers whose values are their keys). Each tile is then read
+// once; every wave parks its K slice in LDS (rows padded by 16 bytes against bank conflicts) and
+// reads it back in the V operand layout.
+template <int D, int G, int SUB, bool SHARED>
 __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1Args a) {
   using Sh = Shape<D>;
   constexpr int kWaves = Sh::kWaves;
@@ -127,6 +130,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   constexpr int kVE = Sh::kVE;
 
   __shared__ __attribute__((aligned(16))) f32x4 score_lds[2][SUB][kWaves][64];
+  constexpr int kKvRow = Sh::kCols + 8;  // padded row of a parked K slice (bf16 elements)
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[SHARED ? kWaves : 1][SUB][16][kKvRow];
 
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
@@ -216,10 +221,13 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
 #pragma unroll
     for (int j = 0; j < kKSteps; ++j)
       r.k[u][j] = load_stream<bf16x8>(a.k_pool + base[u] + k_off + 32 * j);
+  if constexpr (!SHARED) {
 #pragma unroll
-  for (int u = 0; u < SUB; ++u)
+    for (int u = 0; u < SUB; ++u)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[u][i] = load_stream<VRow>(a.v_pool + base[u] + v_off + i * D);
+      for (int i = 0; i < 4; ++i)
+        r.v[u][i] = load_stream<VRow>(a.v_pool + base[u] + v_off + i * D);
+  }
   // A fence the loop latch does not have: otherwise the identical trailing V loads of this
   // prologue and of the loop body get merged into the loop header, which would turn the V
   // prefetch into a load at the top of every step.
@@ -244,6 +252,15 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
           p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[u][j + 1], qop[j + 1], p1, 0, 0, 0);
       }
       score_lds[buf][u][wave][lane] = p0 + p1;
+      if constexpr (SHARED) {
+        // Park this wave's K slice of tile u (row col, columns 32j + 8grp) before the registers
+        // are refilled; P.V reads it back as V.
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j)
+          *reinterpret_cast<bf16x8*>(&kv_lds[SHARED ? wave : 0][u][col][32 * j + 8 * grp]) =
+              r.k[u][j];
+        compiler_fence();
+      }
     }
 
     // Next step's K into the registers just consumed, then the page ids of the step after. The
@@ -328,8 +345,15 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       VRow vr[4];
+      if constexpr (SHARED) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) vr[i] = r.v[u][i];
+        for (int i = 0; i < 4; ++i)
+          vr[i] = *reinterpret_cast<const VRow*>(
+              &kv_lds[SHARED ? wave : 0][u][4 * grp + i][kVE * col]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vr[i] = r.v[u][i];
+      }
       if (!full) {  // masked keys: V := 0 (their p is 0, but 0 * NaN would not be)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -355,11 +379,15 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
 
     // Next step's V into the registers just consumed.
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!SHARED) {
 #pragma unroll
-    for (int u = 0; u < SUB; ++u)
+      for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        r.v[u][i] = load_stream<VRow>(a.v_pool + base_n[u] + v_off + i * D);
+        for (int i = 0; i < 4; ++i)
+          r.v[u][i] = load_stream<VRow>(a.v_pool + base_n[u] + v_off + i * D);
+    } else {
+      compiler_fence();  // this step's LDS reads stay before the next step's writes
+    }
 #pragma unroll
     for (int u = 0; u < SUB; ++u) ok[u] = ok_n[u];
     pid_next = pid_after;
@@ -388,23 +416,25 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
 }
 
 template <int D, int G>
-hipError_t launch(const Stage1Args& args, int batch, hipStream_t stream) {
+hipError_t launch(const Stage1Args& args, bool shared, int batch, hipStream_t stream) {
   constexpr int kSub = DECODE_ATTN_STAGE1_SUB;
   dim3 grid(args.num_splits, args.num_kv_heads, batch);
   dim3 block(Shape<D>::kThreads);
   void* kargs[] = {const_cast<Stage1Args*>(&args)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub>), grid, block,
-                         kargs, 0, stream);
+  const void* fn = shared ? reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, true>)
+                          : reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, false>);
+  return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
 }
 
 template <int D>
-hipError_t launch_d(const Stage1Args& args, int group_size, int batch, hipStream_t stream) {
+hipError_t launch_d(const Stage1Args& args, int group_size, bool shared, int batch,
+                    hipStream_t stream) {
   switch (group_size) {
-    case 1: return launch<D, 1>(args, batch, stream);
-    case 2: return launch<D, 2>(args, batch, stream);
-    case 4: return launch<D, 4>(args, batch, stream);
-    case 8: return launch<D, 8>(args, batch, stream);
-    case 16: return launch<D, 16>(args, batch, stream);
+    case 1: return launch<D, 1>(args, shared, batch, stream);
+    case 2: return launch<D, 2>(args, shared, batch, stream);
+    case 4: return launch<D, 4>(args, shared, batch, stream);
+    case 8: return launch<D, 8>(args, shared, batch, stream);
+    case 16: return launch<D, 16>(args, shared, batch, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -420,9 +450,10 @@ bool stage1_supported(int head_dim, int group_size) {
 
 hipError_t launch_stage1(const Stage1Args& args, int head_dim, int group_size, int batch,
                          hipStream_t stream) {
+  const bool shared = args.k_pool == args.v_pool;
   switch (head_dim) {
-    case 256: return launch_d<256>(args, group_size, batch, stream);
-    case 512: return launch_d<512>(args, group_size, batch, stream);
+    case 256: return launch_d<256>(args, group_size, shared, batch, stream);
+    case 512: return launch_d<512>(args, group_size, shared, batch, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -229,15 +229,16 @@ def make_workload_layer(name: str, kind: str, poison: bool = True) -> LayerInput
 
 
 def algorithmic_bytes(ctx_lens: Sequence[int], num_q_heads: int, num_kv_heads: int, head_dim: int,
-                      page_size: int = 16, window: int = 0) -> int:
-    """Bytes the method must move for one layer call: attended K and V (bf16), q (bf16), out
-    (fp32) and the block-table entries of the pages touched (int32)."""
+                      page_size: int = 16, window: int = 0, k_eq_v: bool = False) -> int:
+    """Bytes the method must move for one layer call: attended K and V (bf16; K only when the
+    values are the keys), q (bf16), out (fp32) and the block-table entries of the pages touched
+    (int32)."""
     kv = 0
     table = 0
     for n in ctx_lens:
         lo, hi = attended_range(int(n), window)
         e = max(0, hi - lo)
-        kv += e * num_kv_heads * head_dim * 2 * 2
+        kv += e * num_kv_heads * head_dim * 2 * (1 if k_eq_v else 2)
         if e:
             table += ((hi - 1) // page_size - lo // page_size + 1) * 4
     B = len(ctx_lens)

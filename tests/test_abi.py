@@ -43,11 +43,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_plan_struct_layout_matches_header():
-    # 12 int32 problem fields, 4 int32, 2 uint64, uint32 magic, 7 int32 reserved (+ padding)
-    assert ctypes.sizeof(binding.Problem) == 48
-    assert binding.Plan.workspace_bytes.offset == 64
-    assert binding.Plan.magic.offset == 80
-    assert ctypes.sizeof(binding.Plan) == 112
+    # 13 int32 problem fields, 4 int32, 2 uint64, uint32 magic, 7 int32 reserved (+ padding)
+    assert ctypes.sizeof(binding.Problem) == 52
+    assert binding.Plan.workspace_bytes.offset == 72
+    assert binding.Plan.magic.offset == 88
+    assert ctypes.sizeof(binding.Plan) == 120
 
 
 def plan(**kw):
@@ -92,6 +92,21 @@ def test_plan_long_context_split_counts_meet_chunk_rules():
                 max_ctx_len=132096).num_splits >= 128
     assert 2 * plan(batch=2, max_pages_per_seq=4160, num_pages=16384,
                     max_ctx_len=66560).num_splits >= 128
+
+
+def test_plan_values_are_keys_doubles_the_workgroups():
+    assert plan(values_are_keys=True).num_splits == 64
+    assert plan(batch=1, max_pages_per_seq=8256, num_pages=16384, max_ctx_len=132096,
+                values_are_keys=True).num_splits == 256
+    prob = binding.Problem(4, 16, 2, 512, 16, 2112, 16896, 33792, 0, 256, 0, 0, 2)
+    out = binding.Plan()
+    assert binding.load_library().decode_attn_plan(ctypes.byref(prob), ctypes.byref(out)) == \
+        ERR_SHAPE
+
+
+def test_values_are_keys_plan_needs_one_pool(lib):
+    p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600, values_are_keys=True)
+    assert call_global(lib, p, k=A, v=A + 4096) == ERR_SHAPE
 
 
 def test_plan_force_and_cap():
@@ -188,6 +203,20 @@ def test_stage_entry_validation(lib):
     assert lib.decode_attn_stage2(ctypes.byref(p), 1, A, p.workspace_bytes, A, A + 2, None) == \
         ERR_ALIGN
     assert lib.decode_attn_stage2(ctypes.byref(p), 0, None, 0, None, None, None) == OK
+
+
+def test_append_validation(lib):
+    p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600)
+    bp = ctypes.byref(p)
+    assert lib.decode_attn_append_kv(bp, None, A, A, A, A, A, 1, None) == ERR_NULL
+    assert lib.decode_attn_append_kv(bp, A, None, A, A + 64, A, A, 1, None) == ERR_NULL
+    assert lib.decode_attn_append_kv(bp, A + 2, A, A, A + 64, A, A, 1, None) == ERR_ALIGN
+    assert lib.decode_attn_append_kv(bp, A, A, A, A + 64, A, A, 3, None) == ERR_SHAPE
+    assert lib.decode_attn_append_kv(bp, None, None, None, None, None, None, 0, None) == OK
+    bad = binding.Plan.from_buffer_copy(p)
+    bad.magic = 1
+    assert lib.decode_attn_append_kv(ctypes.byref(bad), A, A, A, A + 64, A, A, 1, None) == \
+        ERR_PLAN
 
 
 def test_status_strings(lib):

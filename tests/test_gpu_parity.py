@@ -146,3 +146,33 @@ def test_extreme_scores_stay_finite():
     inp = make_layer_inputs([777, 90], 16, 2, 512, page_size=16, seed=19, q_mult=40.0)
     out, lse = gu.run(inp)
     gu.compare(out, lse, *gu.reference(inp), "extreme")
+
+
+@pytest.mark.parametrize("window", [0, 300])
+def test_values_equal_keys_one_pool(window):
+    """Layers whose values are their keys pass the same pool as K and V."""
+    inp = make_layer_inputs([1000, 77, 2049], 16, 2, 512 if window == 0 else 256, page_size=16,
+                            window=window, seed=[31, window])
+    inp.v_pool = inp.k_pool
+    t = gu.upload(inp)
+    t["v"] = t["k"]
+    for flag in (True, False):  # planned as such, or only passed one pool
+        out, lse = gu.run(inp, dev_bufs=t, values_are_keys=flag)
+        gu.compare(out, lse, *gu.reference(inp), "k=v W%d planned %s" % (window, flag))
+
+
+@pytest.mark.parametrize("S,ns", [(256, 3), (1024, 2), (16, 1024)])
+def test_large_pages_and_max_splits(S, ns):
+    """Page sizes up to 1024 keys and the largest split count."""
+    inp = make_layer_inputs([3000, 1, 2500], 8, 2, 512, page_size=S, seed=[32, S])
+    out, lse = gu.run(inp, force_splits=ns)
+    gu.compare(out, lse, *gu.reference(inp), "S%d ns%d" % (S, ns))
+
+
+def test_many_sequences():
+    """A large batch of short ragged sequences (more workgroups than fit the GPU at once)."""
+    rng = np.random.default_rng(33)
+    ctx = rng.integers(1, 700, size=96)
+    inp = make_layer_inputs(ctx, 16, 8, 256, page_size=16, window=512, seed=34)
+    out, lse = gu.run(inp)
+    gu.compare(out, lse, *gu.reference(inp), "batch 96")

@@ -421,3 +421,63 @@ def test_golden_regression_cases():
                                       inp.scale, window=case["window"])
         np.testing.assert_allclose(out, np.array(case["out"]), rtol=0, atol=1e-12)
         np.testing.assert_allclose(lse, np.array(case["lse"]), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- paged KV append
+
+
+def test_append_writes_exactly_the_newest_slot():
+    rng = np.random.default_rng(40)
+    inp = make_layer_inputs([5, 16, 17, 33], 4, 2, 16, page_size=16, seed=41, poison=False)
+    k0, v0 = inp.k_pool.copy(), inp.v_pool.copy()
+    k_new = rand_bits(rng, (4, 2, 16))
+    v_new = rand_bits(rng, (4, 2, 16))
+    oracle.append_kv(k_new, v_new, inp.k_pool, inp.v_pool, inp.block_table, inp.ctx_lens)
+    expect_k, expect_v = k0.copy(), v0.copy()
+    for b, n in enumerate(inp.ctx_lens):
+        t = int(n) - 1
+        page = inp.block_table[b, t // 16]
+        expect_k[page, :, t % 16] = k_new[b]
+        expect_v[page, :, t % 16] = v_new[b]
+    np.testing.assert_array_equal(inp.k_pool, expect_k)
+    np.testing.assert_array_equal(inp.v_pool, expect_v)
+
+
+def test_append_round_trip_restores_attention():
+    """Removing each sequence's newest key/value (NaN) and appending it back gives the original
+    attention output bitwise."""
+    inp = make_layer_inputs([1, 20, 64, 65], 8, 2, 32, page_size=16, seed=42)
+    ref = oracle.decode_attn(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.ctx_lens,
+                             inp.scale)
+    k_new = np.zeros((4, 2, 32), np.uint16)
+    v_new = np.zeros((4, 2, 32), np.uint16)
+    for b, n in enumerate(inp.ctx_lens):
+        t = int(n) - 1
+        page = inp.block_table[b, t // 16]
+        k_new[b] = inp.k_pool[page, :, t % 16]
+        v_new[b] = inp.v_pool[page, :, t % 16]
+        inp.k_pool[page, :, t % 16] = 0x7FC0
+        inp.v_pool[page, :, t % 16] = 0x7FC0
+    oracle.append_kv(k_new, v_new, inp.k_pool, inp.v_pool, inp.block_table, inp.ctx_lens)
+    out = oracle.decode_attn(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.ctx_lens,
+                             inp.scale)
+    np.testing.assert_array_equal(out[0], ref[0])
+    np.testing.assert_array_equal(out[1], ref[1])
+
+
+def test_append_one_pool_writes_keys_only():
+    rng = np.random.default_rng(43)
+    inp = make_layer_inputs([9], 2, 1, 16, page_size=16, seed=44, poison=False)
+    k_new = rand_bits(rng, (1, 1, 16))
+    pool = inp.k_pool
+    oracle.append_kv(k_new, None, pool, pool, inp.block_table, inp.ctx_lens)
+    page = inp.block_table[0, 0]
+    np.testing.assert_array_equal(pool[page, 0, 8], k_new[0, 0])
+
+
+def test_append_rejects_positions_outside_the_table():
+    inp = make_layer_inputs([16], 2, 1, 16, page_size=16, seed=45)
+    ctx = np.array([17], np.int32)  # position 16 needs a second table column that is absent
+    with pytest.raises(ValueError):
+        oracle.append_kv(np.zeros((1, 1, 16), np.uint16), np.zeros((1, 1, 16), np.uint16),
+                         inp.k_pool, inp.v_pool, inp.block_table, ctx)
