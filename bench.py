@@ -70,6 +70,10 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--k-eq-v", action="store_true",
                     help="layers whose values are their keys: one pool passed as both K and V")
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per sequence (causal multi-token decode), both layers")
+    ap.add_argument("--sink", type=int, default=0,
+                    help="sink keys the sliding layer also attends (StreamingLLM-style view)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -109,7 +113,9 @@ def main() -> int:
     for kind in ("global", "sliding"):
         if kind not in wl.layers:
             continue
-        inp = wl_mod.make_workload_layer(args.workload, kind)
+        sink = args.sink if kind == "sliding" else 0
+        inp = wl_mod.make_workload_layer(args.workload, kind, sink=sink, q_len=args.q_len)
+        lead = (inp.dims["B"],) if args.q_len == 1 else (inp.dims["B"], args.q_len)
         d = inp.dims
         bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
             torch.bfloat16)
@@ -123,20 +129,20 @@ def main() -> int:
             vs.append(ks[-1] if args.k_eq_v else v0.clone())
         plan = pda.decode_attn_plan(d["B"], d["Hq"], d["Hkv"], d["D"], d["S"], d["M"], d["P"],
                                     max_ctx_len=int(inp.ctx_lens.max()), window=inp.window,
-                                    values_are_keys=args.k_eq_v)
+                                    values_are_keys=args.k_eq_v, sink=sink, q_len=args.q_len)
         spec = wl.layers[kind]
         layers.append(dict(
             kind=kind, inp=inp, dims=d, plan=plan, q=bf(inp.q), k=ks, v=vs,
             bt=torch.from_numpy(inp.block_table).to(dev),
             ctx=torch.from_numpy(inp.ctx_lens).to(dev),
-            out=torch.empty((d["B"], d["Hq"], d["D"]), device=dev),
-            lse=torch.empty((d["B"], d["Hq"]), device=dev),
+            out=torch.empty(lead + (d["Hq"], d["D"]), device=dev),
+            lse=torch.empty(lead + (d["Hq"],), device=dev),
             ws=torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev),
             bytes=wl_mod.algorithmic_bytes(inp.ctx_lens, spec.num_q_heads, spec.num_kv_heads,
                                            spec.head_dim, wl.page_size, spec.window,
-                                           k_eq_v=args.k_eq_v),
+                                           k_eq_v=args.k_eq_v, sink=sink, q_len=args.q_len),
             flops=wl_mod.algorithmic_flops(inp.ctx_lens, spec.num_q_heads, spec.head_dim,
-                                           spec.window)))
+                                           spec.window, sink=sink, q_len=args.q_len)))
         del inp.k_pool, inp.v_pool  # host copies are regenerated for the CPU leg if needed
     torch.cuda.synchronize()
     print("# inputs ready in %.1f s: %s" % (time.time() - t_gen, ", ".join(
@@ -204,9 +210,10 @@ def main() -> int:
     # (4 * D bytes per key and KV head), q, and the block-table entries of the pages touched.
     ginp = dominant["inp"]
     gd = dominant["dims"]
-    s1_bytes = dominant["bytes"] - gd["B"] * gd["Hq"] * gd["D"] * 4  # minus out (stage 2 writes)
+    s1_bytes = dominant["bytes"] - gd["B"] * args.q_len * gd["Hq"] * gd["D"] * 4  # minus out
     achieved = s1_bytes / (s1_avg_us * 1e-6) / 1e9
-    traffic = load_traffic(args.workload)
+    plain = args.q_len == 1 and args.sink == 0 and not args.k_eq_v
+    traffic = load_traffic(args.workload) if plain else None
 
     result = {
         "metric": METRIC,
@@ -236,6 +243,8 @@ def main() -> int:
             "step_algorithmic_bytes": step_bytes,
             "kv_pool_copies_rotated": R,
             "k_eq_v": bool(args.k_eq_v),
+            "q_len": args.q_len,
+            "sliding_sink": args.sink,
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -257,7 +266,9 @@ def main() -> int:
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
-        host = [wl_mod.make_workload_layer(args.workload, L["kind"]) for L in layers]
+        host = [wl_mod.make_workload_layer(args.workload, L["kind"], q_len=args.q_len,
+                                           sink=args.sink if L["kind"] == "sliding" else 0)
+                for L in layers]
         if args.k_eq_v:
             for h in host:
                 h.v_pool = h.k_pool
@@ -266,8 +277,10 @@ def main() -> int:
         reps, t_cpu, refs = 0, 0.0, None
         while True:
             t_a = time.perf_counter()
-            refs = [oracle.decode_attn(h.q, h.k_pool, h.v_pool, h.block_table, h.ctx_lens,
-                                       h.scale, window=h.window) for h in host]
+            refs = [oracle.decode_attn_multi(h.q if h.q_len > 1 else h.q[:, None], h.k_pool,
+                                             h.v_pool, h.block_table, h.ctx_lens, h.scale,
+                                             h.window, h.sink) for h in host]
+            refs = [r if h.q_len > 1 else (r[0][:, 0], r[1][:, 0]) for h, r in zip(host, refs)]
             t_cpu += time.perf_counter() - t_a
             reps += 1
             if t_cpu >= args.cpu_seconds or reps >= 1000:

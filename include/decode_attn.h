@@ -10,14 +10,21 @@
  * "专用算子与性能优化" / dedicated operators). Decode is one new query token per sequence attending
  * to all of its cached keys (vLLM learning notes "模型库与算子层 — 概念", section "核心操作").
  *
- * For sequence b, query head h, KV head g = h / G (G = Hq / Hkv, contiguous groups):
- *     n   = ctx_lens[b]                      (keys cached for b, the new token included)
+ * For sequence b, query token i < L (L = q_len, 1 for plain decode), query head h, KV head
+ * g = h / G (G = Hq / Hkv, contiguous groups):
+ *     n   = ctx_lens[b] - L + i + 1          (keys visible to the query: the cached keys up to
+ *                                             and including its own position n - 1)
  *     lo  = 0 (global)  or  max(0, n - W) (sliding)
- *     s_t = scale * <q[b,h,:], K_t>          for t in [lo, n)
- *     out[b,h,:] = sum_t exp(s_t - m) V_t / sum_t exp(s_t - m),   m = max_t s_t
- *     lse[b,h]   = m + ln(sum_t exp(s_t - m))
- * where K_t / V_t live in pool page block_table[b, t / S] at slot t % S. n == 0 gives out = 0 and
- * lse = -inf.
+ *     A   = [lo, n), plus [0, min(sink, n)) for a sliding layer planned with sink > 0
+ *     s_t = scale * <q[b,i,h,:], K_t>        for t in A
+ *     out[b,i,h,:] = sum_t exp(s_t - m) V_t / sum_t exp(s_t - m),   m = max_t s_t
+ *     lse[b,i,h]   = m + ln(sum_t exp(s_t - m))
+ * where K_t / V_t live in pool page block_table[b, t / S] at slot t % S. An empty A (n <= 0)
+ * gives out = 0 and lse = -inf. The sink keys give the StreamingLLM-style views the same page
+ * supports (section "Gemma 4 文本推理"): a window of recent keys plus a few leading ones. L > 1
+ * is causal multi-token verification (the last L cached keys are the new tokens themselves; vLLM
+ * learning notes, the MLA backend notes on causal multi-token verification); L = 1 is the
+ * single-token decode that section "核心操作" of the same notes describes.
  *
  * How. Split-KV: stage 1 cuts each sequence's key range into num_splits chunks and writes, per
  * (b, h, split), the chunk's normalised partial output and its log-sum-exp; stage 2 merges the
@@ -30,17 +37,20 @@
  * "专用算子与性能优化", plan invalidation on page-table address change).
  *
  * Layouts (all row-major, contiguous, device memory):
- *     q            [B, Hq, D]             bf16
+ *     q            [B, L, Hq, D]          bf16   ([B, Hq, D] when L = 1)
  *     k_pool       [P, Hkv, S, D]         bf16   one (page, kv head) block is S*D contiguous values
  *     v_pool       [P, Hkv, S, D]         bf16   the same buffer as k_pool for layers whose values
  *                                                are their keys (K = V, Sparse-vLLM PR #27, section
  *                                                "Gemma 4 文本推理"): plan them with
  *                                                values_are_keys = 1 and pass one pool twice
  *     block_table  [B, max_pages_per_seq] int32  physical page ids; entries of pages holding no key
- *                                                in [lo, n) are never read and may hold anything
+ *                                                of A are never read and may hold anything. A
+ *                                                sparse view (a table naming only some of a
+ *                                                sequence's pages, n counting the keys they hold)
+ *                                                is attended like any other table
  *     ctx_lens     [B]                    int32
- *     out          [B, Hq, D]             fp32
- *     lse_out      [B, Hq]                fp32   (optional, may be NULL)
+ *     out          [B, L, Hq, D]          fp32
+ *     lse_out      [B, L, Hq]             fp32   (optional, may be NULL)
  *     workspace    workspace_bytes bytes  stage-1 partials, see decode_attn_stage1
  *
  * Ownership and threading. Every buffer is owned by the caller; the library never allocates or
@@ -79,10 +89,11 @@ typedef enum {
 
 /* Compiled kernel variants. */
 #define DECODE_ATTN_MAX_SPLITS_LIMIT 1024 /* hard upper bound on num_splits */
+#define DECODE_ATTN_MAX_Q_LEN 16          /* most query tokens per sequence in one call */
 
 /* The shape a plan covers. Values are upper bounds for the calls made with the plan. */
 typedef struct {
-  int32_t batch;             /* B >= 1: most sequences per call */
+  int32_t batch;             /* B >= 1: most sequences per call; B * max(1, q_len) <= 65535 */
   int32_t num_q_heads;       /* Hq >= 1 */
   int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0; G = Hq / Hkv in {1, 2, 4, 8, 16} */
   int32_t head_dim;          /* D in {256, 512} */
@@ -97,6 +108,12 @@ typedef struct {
   int32_t force_splits;      /* 0 = the planner chooses; > 0 = use exactly this many (<= 1024) */
   int32_t values_are_keys;   /* 1: the layer's values are its keys and calls pass one pool as both
                                 k_pool and v_pool (each tile is then read once); 0: separate pools */
+  int32_t sink;              /* sliding layers only: also attend the first `sink` keys of every
+                                sequence (attention sinks of StreamingLLM-style views); 0 = none.
+                                Ignored when window == 0, where every key is attended anyway */
+  int32_t q_len;             /* L: new query tokens per sequence, 0 or 1 = single-token decode,
+                                up to DECODE_ATTN_MAX_Q_LEN (speculative verification, short
+                                chunks); every call with the plan passes L tokens per sequence */
 } decode_attn_problem;
 
 /* A plan: plain data, copy it freely; there is nothing to free. */
@@ -115,10 +132,11 @@ typedef struct {
 /*
  * decode_attn_plan — host only, no device work (a device query only when problem->num_cus == 0).
  * Checks the problem, picks the split count and computes the workspace size.
- * Split rule: with T = ceil(e / 16) (+ 1 for a sliding window, whose edge may straddle a tile)
- * tiles of 16 keys for the longest attended range
- * e = min(max_ctx_len, W or unlimited), pairs = batch * Hkv and target = num_cus workgroups for
- * head_dim 512 with separate pools (2 * num_cus for head_dim 256 or when values are keys),
+ * Split rule: with T = ceil(e / 16) (+ 1 for a sliding window, whose edge may straddle a tile,
+ * + ceil(sink / 16) for its sink keys) tiles of 16 keys for the longest range one query block
+ * walks, e = min(max_ctx_len, W + min(L, 16 / G) - 1 or unlimited),
+ * pairs = batch * Hkv * ceil(L / (16 / G)) and target = num_cus workgroups for head_dim 512 with
+ * separate pools (2 * num_cus for head_dim 256 or when values are keys),
  *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, ceil(T / 2)))
  * so every chunk holds at least 2 tiles (32 keys, one stage-1 loop step) when the context
  * allows it.
@@ -142,8 +160,9 @@ int decode_attn_global(const decode_attn_plan_t* plan, const void* q, const void
 /*
  * decode_attn_sliding — attention of a sliding-window layer: the same call as decode_attn_global
  * plus `window`, which must equal plan->problem.window (> 0). Only keys t with
- * max(0, n - window) <= t < n are read; window edges need not fall on 16- or 32-key boundaries
- * (Sparse-vLLM PR #27, section "专用算子与性能优化", non-32-aligned blocks of the sliding kernel).
+ * max(0, n - window) <= t < n, and t < plan->problem.sink, are read; window and sink edges need
+ * not fall on 16- or 32-key boundaries (Sparse-vLLM PR #27, section "专用算子与性能优化",
+ * non-32-aligned blocks of the sliding kernel).
  */
 int decode_attn_sliding(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
                         const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
@@ -153,11 +172,14 @@ int decode_attn_sliding(const decode_attn_plan_t* plan, const void* q, const voi
 /*
  * decode_attn_stage1 — stage 1 alone, for either layer kind (the window comes from the plan).
  * Writes the workspace, which holds two planes:
- *     o_part [B, Hq, num_splits, D] fp32 at byte offset 0
- *     lse    [B, Hq, num_splits]    fp32 at byte offset plan->partial_lse_offset
- * Split s of sequence b covers the 16-key tiles [floor(s*T_b/ns), floor((s+1)*T_b/ns)) of the
- * tiles overlapping [lo, n), counted from tile floor(lo/16) (T_b tiles, ns = num_splits); keys
- * outside [lo, n) are masked. o_part is that chunk's softmax-normalised output and lse its
+ *     o_part [B, L, Hq, num_splits, D] fp32 at byte offset 0
+ *     lse    [B, L, Hq, num_splits]    fp32 at byte offset plan->partial_lse_offset
+ * The queries of a sequence are taken in blocks of 16 / G (one block when L = 1). Split s of a
+ * block covers the tiles [floor(s*T/ns), floor((s+1)*T/ns)) of the block's list of T 16-key
+ * tiles (ns = num_splits). With lo and n those of the block's first and last query respectively,
+ * the list holds the tiles 0 .. ceil(k/16) - 1 that overlap the sink keys [0, k), k = min(sink,
+ * lo), followed by the tiles overlapping [lo, n) not already listed; keys outside a query's A
+ * are masked for it. o_part is that chunk's softmax-normalised output and lse its
  * log-sum-exp of s_t; a chunk with no key has o_part = 0 and lse = -inf. Together with
  * decode_attn_stage2 this lets the partials be produced and merged separately (for example by
  * different devices that each own part of the pages).
@@ -176,15 +198,17 @@ int decode_attn_stage2(const decode_attn_plan_t* plan, int32_t batch, const void
                        uint64_t workspace_bytes, float* out, float* lse_out, void* stream);
 
 /*
- * decode_attn_append_kv — write each sequence's newest key and value into the paged pools before
- * attention reads them (the cache-manager write of Sparse-vLLM PR #27, section
- * "Gemma 4 文本推理"; ctx_lens counts the new token). For b < batch with n = ctx_lens[b] >= 1,
- * token t = n - 1 goes to page block_table[b, t / S], slot t % S, for every KV head g:
- *     k_pool[page, g, t % S, :] = k_new[b, g, :]    and the same for V.
- * k_new, v_new: [B, Hkv, D] bf16, 16-byte aligned. v_pool may equal k_pool (layers whose values
- * are their keys): then only k_new is written and v_new may be NULL. A position outside the
- * table row or a page id outside [0, P) is skipped (nothing written for that sequence). Any plan
- * of the layer can be used (only its shape is read). Bitwise copy; asynchronous on `stream`.
+ * decode_attn_append_kv — write each sequence's L = plan->problem.q_len newest keys and values
+ * into the paged pools before attention reads them (the cache-manager write of Sparse-vLLM PR #27,
+ * section "Gemma 4 文本推理"; ctx_lens counts the new tokens). For b < batch, n = ctx_lens[b] and
+ * i < L, the token at position t = n - L + i (skipped if t < 0) goes to page
+ * block_table[b, t / S], slot t % S, for every KV head g:
+ *     k_pool[page, g, t % S, :] = k_new[b, i, g, :]    and the same for V.
+ * k_new, v_new: [B, L, Hkv, D] bf16 ([B, Hkv, D] when L = 1), 16-byte aligned. v_pool may equal
+ * k_pool (layers whose values are their keys): then only k_new is written and v_new may be NULL.
+ * A position outside the table row or a page id outside [0, P) is skipped (nothing written for
+ * that token). Any plan of the layer with the same q_len can be used (only its shape is read).
+ * Bitwise copy; asynchronous on `stream`.
  */
 int decode_attn_append_kv(const decode_attn_plan_t* plan, const void* k_new, const void* v_new,
                           void* k_pool, void* v_pool, const int32_t* block_table,

@@ -57,7 +57,11 @@ def _load():
     lib.oracle_lse_merge.restype = ctypes.c_int
     lib.oracle_key_range.argtypes = [i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.oracle_key_range.restype = None
-    lib.oracle_append_kv.argtypes = [i32] * 6 + [vp] * 6
+    lib.oracle_decode_attn_sink.argtypes = [i32] * 7 + [vp] * 5 + [i32, i32, f64, vp, vp, i32]
+    lib.oracle_decode_attn_sink.restype = ctypes.c_int
+    lib.oracle_decode_attn_multi.argtypes = [i32] * 8 + [vp] * 5 + [i32, i32, f64, vp, vp, i32]
+    lib.oracle_decode_attn_multi.restype = ctypes.c_int
+    lib.oracle_append_kv.argtypes = [i32] * 7 + [vp] * 6
     lib.oracle_append_kv.restype = ctypes.c_int
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
@@ -112,6 +116,47 @@ def decode_attn(q, k_pool, v_pool, block_table, ctx_lens, scale, window=0, num_t
     return out, lse
 
 
+def decode_attn_sink(q, k_pool, v_pool, block_table, ctx_lens, scale, window, sink,
+                     num_threads=0):
+    """Oracle output of a sliding layer that also attends the first ``sink`` keys."""
+    lib = _load()
+    q, k_pool, v_pool = _bits(q), _bits(k_pool), _bits(v_pool)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx_lens = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    B, Hq, Hkv, D, S, P, M = _check_shapes(q, k_pool, v_pool, block_table)
+    out = np.zeros((B, Hq, D), dtype=np.float64)
+    lse = np.zeros((B, Hq), dtype=np.float64)
+    rc = lib.oracle_decode_attn_sink(B, Hq, Hkv, D, S, M, P, _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                     _ptr(block_table), _ptr(ctx_lens), int(window), int(sink),
+                                     float(scale), _ptr(out), _ptr(lse), int(num_threads))
+    if rc != 0:
+        raise ValueError("oracle_decode_attn_sink failed with code %d" % rc)
+    return out, lse
+
+
+def decode_attn_multi(q, k_pool, v_pool, block_table, ctx_lens, scale, window=0, sink=0,
+                      num_threads=0):
+    """Oracle output ``(out[B,L,Hq,D], lse[B,L,Hq])`` of L new tokens per sequence (``q`` is
+    [B, L, Hq, D]); query i sits at position ctx_lens[b] - L + i and attends causally."""
+    lib = _load()
+    q, k_pool, v_pool = _bits(q), _bits(k_pool), _bits(v_pool)
+    block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+    ctx_lens = np.ascontiguousarray(ctx_lens, dtype=np.int32)
+    if q.ndim != 4:
+        raise ValueError("q must be [B, L, Hq, D]")
+    B, L, Hq, D = q.shape
+    _, _, Hkv, _, S, P, M = _check_shapes(q[:, 0], k_pool, v_pool, block_table)
+    out = np.zeros((B, L, Hq, D), dtype=np.float64)
+    lse = np.zeros((B, L, Hq), dtype=np.float64)
+    rc = lib.oracle_decode_attn_multi(B, L, Hq, Hkv, D, S, M, P, _ptr(q), _ptr(k_pool),
+                                      _ptr(v_pool), _ptr(block_table), _ptr(ctx_lens), int(window),
+                                      int(sink), float(scale), _ptr(out), _ptr(lse),
+                                      int(num_threads))
+    if rc != 0:
+        raise ValueError("oracle_decode_attn_multi failed with code %d" % rc)
+    return out, lse
+
+
 def decode_attn_ranges(q, k_pool, v_pool, block_table, key_lo, key_hi, scale, num_threads=0):
     """Oracle output over explicit per-sequence key ranges ``[key_lo[b], key_hi[b])``."""
     lib = _load()
@@ -147,7 +192,8 @@ def lse_merge(o_parts, lses):
 
 
 def append_kv(k_new, v_new, k_pool, v_pool, block_table, ctx_lens):
-    """Write each sequence's newest token (position ctx_lens[b] - 1) into the pools, in place.
+    """Write each sequence's newest token (position ctx_lens[b] - 1) into the pools, in place;
+    ``k_new`` [B, Hkv, D], or [B, L, Hkv, D] for the L newest tokens (positions n - L .. n - 1).
     ``v_pool is k_pool`` writes K only (layers whose values are their keys)."""
     lib = _load()
     same = v_pool is k_pool
@@ -156,11 +202,17 @@ def append_kv(k_new, v_new, k_pool, v_pool, block_table, ctx_lens):
             raise TypeError("bf16 bit patterns (uint16), C-contiguous, expected")
     block_table = np.ascontiguousarray(block_table, dtype=np.int32)
     ctx_lens = np.ascontiguousarray(ctx_lens, dtype=np.int32)
-    B, Hkv, D = k_new.shape
+    if k_new.ndim == 3:
+        B, Hkv, D = k_new.shape
+        L = 1
+    else:
+        B, L, Hkv, D = k_new.shape
+    if not same and v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new differ in shape")
     P, Hkv2, S, D2 = k_pool.shape
     if Hkv2 != Hkv or D2 != D or block_table.shape[0] != B:
         raise ValueError("inconsistent shapes")
-    rc = lib.oracle_append_kv(B, Hkv, D, S, block_table.shape[1], P, _ptr(k_new),
+    rc = lib.oracle_append_kv(B, L, Hkv, D, S, block_table.shape[1], P, _ptr(k_new),
                               _ptr(k_new if same else v_new), _ptr(k_pool),
                               _ptr(k_pool if same else v_pool), _ptr(block_table), _ptr(ctx_lens))
     if rc != 0:

@@ -43,7 +43,7 @@ class Problem(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in (
         "batch", "num_q_heads", "num_kv_heads", "head_dim", "page_size", "max_pages_per_seq",
         "num_pages", "max_ctx_len", "window", "num_cus", "max_splits", "force_splits",
-        "values_are_keys")]
+        "values_are_keys", "sink", "q_len")]
 
 
 class Plan(ctypes.Structure):
@@ -147,6 +147,30 @@ def _nbytes(x) -> int:
     return x.numel() * x.element_size()
 
 
+def _need(x, name: str, elems: int) -> None:
+    """Reject a tensor with fewer elements than the call reads or writes through it (integer
+    addresses are passed through unchecked)."""
+    if x is None or isinstance(x, int):
+        return
+    if x.numel() < elems:
+        raise ValueError("%s holds %d elements, the call needs %d" % (name, x.numel(), elems))
+
+
+def _check_sizes(plan, batch, q=None, k_pool=None, v_pool=None, block_table=None, ctx_lens=None,
+                 out=None, lse_out=None) -> None:
+    p = plan.problem
+    L = max(1, p.q_len)
+    rows = int(batch) * L * p.num_q_heads
+    pool = p.num_pages * p.num_kv_heads * p.page_size * p.head_dim
+    _need(q, "q", rows * p.head_dim)
+    _need(k_pool, "k_pool", pool)
+    _need(v_pool, "v_pool", pool)
+    _need(block_table, "block_table", int(batch) * p.max_pages_per_seq)
+    _need(ctx_lens, "ctx_lens", int(batch))
+    _need(out, "out", rows * p.head_dim)
+    _need(lse_out, "lse_out", rows)
+
+
 def _stream_handle(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -160,12 +184,13 @@ def _stream_handle(stream) -> Optional[int]:
 
 def decode_attn_plan(batch, num_q_heads, num_kv_heads, head_dim, page_size, max_pages_per_seq,
                      num_pages, max_ctx_len=0, window=0, num_cus=0, max_splits=0,
-                     force_splits=0, values_are_keys=False) -> Plan:
+                     force_splits=0, values_are_keys=False, sink=0, q_len=0) -> Plan:
     """Host-only planning (see decode_attn_plan in the header). Returns the plan struct."""
     lib = load_library()
     prob = Problem(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim), int(page_size),
                    int(max_pages_per_seq), int(num_pages), int(max_ctx_len), int(window),
-                   int(num_cus), int(max_splits), int(force_splits), int(bool(values_are_keys)))
+                   int(num_cus), int(max_splits), int(force_splits), int(bool(values_are_keys)),
+                   int(sink), int(q_len))
     plan = Plan()
     _check(lib.decode_attn_plan(ctypes.byref(prob), ctypes.byref(plan)), "decode_attn_plan")
     return plan
@@ -195,6 +220,7 @@ def _ws(workspace, workspace_bytes):
 def decode_attn_global(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, out,
                        lse_out=None, workspace=None, workspace_bytes=None, stream=None) -> None:
     lib = load_library()
+    _check_sizes(plan, batch, q, k_pool, v_pool, block_table, ctx_lens, out, lse_out)
     ws, wsb = _ws(workspace, workspace_bytes)
     _check(lib.decode_attn_global(
         ctypes.byref(plan), _dev_ptr(q, "q", _bf16()), _dev_ptr(k_pool, "k_pool", _bf16()),
@@ -208,6 +234,7 @@ def decode_attn_sliding(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, ba
                         out, lse_out=None, workspace=None, workspace_bytes=None,
                         stream=None) -> None:
     lib = load_library()
+    _check_sizes(plan, batch, q, k_pool, v_pool, block_table, ctx_lens, out, lse_out)
     ws, wsb = _ws(workspace, workspace_bytes)
     _check(lib.decode_attn_sliding(
         ctypes.byref(plan), _dev_ptr(q, "q", _bf16()), _dev_ptr(k_pool, "k_pool", _bf16()),
@@ -220,6 +247,7 @@ def decode_attn_sliding(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, ba
 def decode_attn_stage1(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale,
                        workspace, workspace_bytes=None, stream=None) -> None:
     lib = load_library()
+    _check_sizes(plan, batch, q, k_pool, v_pool, block_table, ctx_lens)
     ws, wsb = _ws(workspace, workspace_bytes)
     _check(lib.decode_attn_stage1(
         ctypes.byref(plan), _dev_ptr(q, "q", _bf16()), _dev_ptr(k_pool, "k_pool", _bf16()),
@@ -231,6 +259,7 @@ def decode_attn_stage1(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, bat
 def decode_attn_stage2(plan: Plan, batch, workspace, out, lse_out=None, workspace_bytes=None,
                        stream=None) -> None:
     lib = load_library()
+    _check_sizes(plan, batch, out=out, lse_out=lse_out)
     ws, wsb = _ws(workspace, workspace_bytes)
     _check(lib.decode_attn_stage2(
         ctypes.byref(plan), int(batch), ws, wsb, _dev_ptr(out, "out", _f32()),
@@ -239,9 +268,16 @@ def decode_attn_stage2(plan: Plan, batch, workspace, out, lse_out=None, workspac
 
 def decode_attn_append_kv(plan: Plan, k_new, v_new, k_pool, v_pool, block_table, ctx_lens, batch,
                           stream=None) -> None:
-    """Write each sequence's newest K/V (position ctx_lens[b] - 1) into the pools. Passing the
-    same tensor as k_pool and v_pool writes K only (v_new may be None)."""
+    """Write each sequence's L = plan q_len newest K/V (positions ctx_lens[b] - L ..) into the
+    pools. Passing the same tensor as k_pool and v_pool writes K only (v_new may be None)."""
     lib = load_library()
+    p = plan.problem
+    new = int(batch) * max(1, p.q_len) * p.num_kv_heads * p.head_dim
+    _need(k_new, "k_new", new)
+    if v_pool is not k_pool:
+        _need(v_new, "v_new", new)
+    _check_sizes(plan, batch, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
+                 ctx_lens=ctx_lens)
     _check(lib.decode_attn_append_kv(
         ctypes.byref(plan), _dev_ptr(k_new, "k_new", _bf16()), _dev_ptr(v_new, "v_new", _bf16()),
         _dev_ptr(k_pool, "k_pool", _bf16()), _dev_ptr(v_pool, "v_pool", _bf16()),

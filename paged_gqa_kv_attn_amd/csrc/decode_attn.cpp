@@ -38,10 +38,21 @@ int query_num_cus(int* cus) {
 
 uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 
-// Workspace layout: o_part [B, Hq, ns, D] fp32, then (256-byte aligned) lse [B, Hq, ns] fp32.
+// Query tokens per sequence of a resolved problem (0 means 1).
+int q_len_of(const decode_attn_problem& p) { return p.q_len > 1 ? p.q_len : 1; }
+
+// Query blocks per (sequence, kv head): the 16 MFMA rows hold 16 / G queries of G heads each.
+int qblocks_of(const decode_attn_problem& p, int group_size) {
+  const int per_block = 16 / group_size;
+  return (q_len_of(p) + per_block - 1) / per_block;
+}
+
+// Workspace layout: o_part [B, L, Hq, ns, D] fp32, then (256-byte aligned) lse [B, L, Hq, ns]
+// fp32.
 void workspace_layout(const decode_attn_problem& p, int num_splits, uint64_t* lse_offset,
                       uint64_t* total) {
-  const uint64_t rows = (uint64_t)p.batch * (uint64_t)p.num_q_heads * (uint64_t)num_splits;
+  const uint64_t rows = (uint64_t)p.batch * (uint64_t)q_len_of(p) * (uint64_t)p.num_q_heads *
+                        (uint64_t)num_splits;
   *lse_offset = align_up(rows * (uint64_t)p.head_dim * 4u, 256);
   *total = align_up(*lse_offset + rows * 4u, 256);
 }
@@ -55,7 +66,8 @@ int check_plan(const decode_attn_plan_t* plan) {
   const decode_attn_problem& p = plan->problem;
   if (p.batch < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1 ||
       p.num_q_heads % p.num_kv_heads != 0 || p.page_size < kTile || p.page_size % kTile != 0 ||
-      p.max_pages_per_seq < 1 || p.num_pages < 1 || p.window < 0 ||
+      p.max_pages_per_seq < 1 || p.num_pages < 1 || p.window < 0 || p.sink < 0 ||
+      p.q_len < 0 || p.q_len > DECODE_ATTN_MAX_Q_LEN ||
       (p.values_are_keys != 0 && p.values_are_keys != 1))
     return DECODE_ATTN_ERR_PLAN;
   if (plan->group_size != p.num_q_heads / p.num_kv_heads) return DECODE_ATTN_ERR_PLAN;
@@ -116,6 +128,9 @@ int run_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool
   a.max_pages_per_seq = p.max_pages_per_seq;
   a.num_pages = p.num_pages;
   a.window = p.window;
+  a.sink = p.window > 0 ? p.sink : 0;
+  a.q_len = q_len_of(p);
+  a.num_qblocks = qblocks_of(p, plan->group_size);
   a.num_splits = plan->num_splits;
   a.scale_log2 = scale * 1.442695040888963407360f;
   if (launch_stage1(a, p.head_dim, plan->group_size, batch, stream) != hipSuccess)
@@ -135,7 +150,7 @@ int run_stage2(const decode_attn_plan_t* plan, int32_t batch, const void* worksp
   a.num_q_heads = p.num_q_heads;
   a.head_dim = p.head_dim;
   a.num_splits = plan->num_splits;
-  if (launch_stage2(a, batch, stream) != hipSuccess) return DECODE_ATTN_ERR_HIP;
+  if (launch_stage2(a, batch * q_len_of(p), stream) != hipSuccess) return DECODE_ATTN_ERR_HIP;
   return DECODE_ATTN_OK;
 }
 
@@ -169,13 +184,16 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   decode_attn_problem p = *problem;
   if (p.batch < 1 || p.num_q_heads < 1 || p.num_kv_heads < 1 || p.head_dim < 1 ||
       p.page_size < 1 || p.max_pages_per_seq < 1 || p.num_pages < 1 || p.max_ctx_len < 0 ||
-      p.window < 0 || p.num_cus < 0 || p.max_splits < 0 || p.force_splits < 0 ||
+      p.window < 0 || p.num_cus < 0 || p.max_splits < 0 || p.force_splits < 0 || p.sink < 0 ||
+      p.q_len < 0 || p.q_len > DECODE_ATTN_MAX_Q_LEN ||
       (p.values_are_keys != 0 && p.values_are_keys != 1))
     return DECODE_ATTN_ERR_SHAPE;
   if (p.num_q_heads % p.num_kv_heads != 0) return DECODE_ATTN_ERR_SHAPE;
   if (p.max_splits > DECODE_ATTN_MAX_SPLITS_LIMIT || p.force_splits > DECODE_ATTN_MAX_SPLITS_LIMIT)
     return DECODE_ATTN_ERR_SHAPE;
   if ((int64_t)p.max_pages_per_seq * p.page_size > INT32_MAX) return DECODE_ATTN_ERR_SHAPE;
+  // Launch grids put (sequence, query token) pairs on a grid dimension capped at 65535.
+  if ((int64_t)p.batch * (p.q_len > 1 ? p.q_len : 1) > 65535) return DECODE_ATTN_ERR_SHAPE;
   const int G = p.num_q_heads / p.num_kv_heads;
   if (p.page_size % kTile != 0 || p.page_size > 1024) return DECODE_ATTN_ERR_UNSUPPORTED;
   if (!stage1_supported(p.head_dim, G)) return DECODE_ATTN_ERR_UNSUPPORTED;
@@ -184,13 +202,17 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
     if (rc != DECODE_ATTN_OK) return rc;
   }
   if (p.max_splits == 0) p.max_splits = kDefaultMaxSplits;
+  if (p.q_len == 0) p.q_len = 1;
 
-  // Longest key range one sequence can attend, in 16-key tiles (a window may straddle one more).
+  // Longest key range one workgroup walks, in 16-key tiles (a window may straddle one more;
+  // sink keys add their own tiles; the queries of a block widen a window by up to 16 / G - 1).
   const int64_t max_keys = (int64_t)p.max_pages_per_seq * p.page_size;
   int64_t e = p.max_ctx_len > 0 ? (p.max_ctx_len < max_keys ? p.max_ctx_len : max_keys) : max_keys;
-  if (p.window > 0 && e > p.window) e = p.window;
-  const int64_t tiles = (e + kTile - 1) / kTile + (p.window > 0 ? 1 : 0);
-  const int64_t pairs = (int64_t)p.batch * p.num_kv_heads;
+  const int64_t span = (int64_t)p.window + (p.q_len < 16 / G ? p.q_len : 16 / G) - 1;
+  if (p.window > 0 && e > span) e = span;
+  int64_t tiles = (e + kTile - 1) / kTile + (p.window > 0 ? 1 : 0);
+  if (p.window > 0) tiles += ((int64_t)(p.sink < max_keys ? p.sink : max_keys) + kTile - 1) / kTile;
+  const int64_t pairs = (int64_t)p.batch * p.num_kv_heads * qblocks_of(p, G);
   // Workgroups to aim for: one per CU for head_dim 512 (a workgroup streams one chunk with 4
   // waves; measured on MI355X, 1 per CU is as fast as 2 and beats 1.5 or 3), two per CU for
   // smaller heads (short per-workgroup chunks, more latency to hide).
@@ -286,6 +308,7 @@ int decode_attn_append_kv(const decode_attn_plan_t* plan, const void* k_new, con
   a.page_size = p.page_size;
   a.max_pages_per_seq = p.max_pages_per_seq;
   a.num_pages = p.num_pages;
+  a.q_len = q_len_of(p);
   if (launch_append(a, batch, static_cast<hipStream_t>(stream)) != hipSuccess)
     return DECODE_ATTN_ERR_HIP;
   return DECODE_ATTN_OK;

@@ -29,6 +29,9 @@ struct Stage1Args {
   int32_t max_pages_per_seq;
   int32_t num_pages;
   int32_t window;               // 0 = all keys
+  int32_t sink;                 // leading keys also attended by a sliding layer (0 = none)
+  int32_t q_len;                // L >= 1 query tokens per sequence (q is [B, L, Hq, D])
+  int32_t num_qblocks;          // ceil(L / (16 / G)): query blocks of one (sequence, kv head)
   int32_t num_splits;
   float scale_log2;             // scale * log2(e): scores in base-2 units
 };
@@ -46,8 +49,8 @@ struct Stage2Args {
 
 // Kernel arguments of the paged KV append (one workgroup per (sequence, KV head)).
 struct AppendArgs {
-  const uint16_t* k_new;        // [B, Hkv, D] bf16
-  const uint16_t* v_new;        // [B, Hkv, D] bf16 (unused when v_pool == k_pool)
+  const uint16_t* k_new;        // [B, L, Hkv, D] bf16
+  const uint16_t* v_new;        // [B, L, Hkv, D] bf16 (unused when v_pool == k_pool)
   uint16_t* k_pool;             // [P, Hkv, S, D] bf16
   uint16_t* v_pool;             // [P, Hkv, S, D] bf16, may equal k_pool
   const int32_t* block_table;   // [B, max_pages_per_seq]
@@ -57,6 +60,7 @@ struct AppendArgs {
   int32_t page_size;
   int32_t max_pages_per_seq;
   int32_t num_pages;
+  int32_t q_len;                // L >= 1 new tokens per sequence
 };
 
 // Launchers (stage1.hip / stage2.hip / append.hip). They return the launch status only. Stage 1

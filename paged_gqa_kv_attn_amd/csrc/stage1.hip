@@ -133,7 +133,9 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   constexpr int kKvRow = Sh::kCols + 8;  // padded row of a parked K slice (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[SHARED ? kWaves : 1][SUB][16][kKvRow];
 
-  const int split = blockIdx.x;
+  const int ns = a.num_splits;
+  const int split = blockIdx.x % ns;
+  const int qb = blockIdx.x / ns;  // query block: queries [qb * kQB, qb * kQB + kQB)
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -141,46 +143,74 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   const int grp = lane >> 4;  // lane group 0..3
   const int col = lane & 15;  // column (scores: head; P.V: column block)
   const int S = a.page_size;
-  const int ns = a.num_splits;
   constexpr int kCols = Sh::kCols;
   using VRow = typename Sh::VRow;
   const int c0 = wave * kCols;  // first head-dim column of this wave
-  const size_t row0 = (size_t)b * a.num_q_heads + (size_t)kvh * G;
+  const int L = a.q_len;
 
-  // Key range of this sequence and the tiles of this split.
+  // The 16 MFMA rows: row r is query qb * kQB + r / G of the sequence, head kvh * G + r % G.
+  // Output row index (b, query, head) in the [B, L, Hq] order of q and of the partials.
+  constexpr int kQB = 16 / G;
+  auto row_query = [&](int r) { return qb * kQB + r / G; };
+  auto row_valid = [&](int r) { return row_query(r) < L; };
+  auto out_row = [&](int r) -> size_t {
+    return ((size_t)b * L + row_query(r)) * a.num_q_heads + (size_t)kvh * G + r % G;
+  };
+
+  // Keys of this sequence: [0, sk) (sink keys not inside the window) and [lo, n). They are walked
+  // as a list of T tiles, list index v: the sink tiles 0 .. st-1 first, then the window's tiles
+  // from physical tile w0 = max(st, lo / 16) on, i.e. physical tile v + (v >= st ? shift : 0).
+  // This split takes list entries [t_begin, t_end).
+  //
+  // Query i of the sequence sits at position n - L + i and attends keys t < n_i = n - L + i + 1,
+  // t >= lo_i (its window), or t < sink. The workgroup walks the union over its queries: the
+  // window of its first query up to n_i of its last one.
   const int max_keys = a.max_pages_per_seq * S;
-  int n = load_uniform(a.ctx_lens, b);
-  n = n < 0 ? 0 : (n > max_keys ? max_keys : n);
-  const int lo = (a.window > 0 && n > a.window) ? n - a.window : 0;
-  const int tile_lo = lo / kTile;
+  int n_ctx = load_uniform(a.ctx_lens, b);
+  n_ctx = n_ctx < 0 ? 0 : (n_ctx > max_keys ? max_keys : n_ctx);
+  auto query_end = [&](int i) { const int e = n_ctx - L + i + 1; return e < 0 ? 0 : e; };
+  auto window_lo = [&](int e) { return (a.window > 0 && e > a.window) ? e - a.window : 0; };
+  const int q_last = (qb + 1) * kQB < L ? (qb + 1) * kQB - 1 : L - 1;
+  const int n = query_end(q_last);
+  const int lo = window_lo(query_end(qb * kQB));
+  const int sk = a.sink < lo ? a.sink : lo;
+  // This lane's row (scores and softmax use row = col).
+  const int row_n = row_valid(col) ? query_end(row_query(col)) : 0;
+  const int row_lo = window_lo(row_n);
+  const int st = (sk + kTile - 1) / kTile;
+  const int w0 = st > lo / kTile ? st : lo / kTile;
   const int tile_hi = (n + kTile - 1) / kTile;
-  const int T = tile_hi > tile_lo ? tile_hi - tile_lo : 0;
-  const int t_begin = tile_lo + (int)(((int64_t)split * T) / ns);
-  const int t_end = tile_lo + (int)(((int64_t)(split + 1) * T) / ns);
+  const int T = st + (tile_hi > w0 ? tile_hi - w0 : 0);
+  const int shift = w0 - st;
+  const int t_begin = (int)(((int64_t)split * T) / ns);
+  const int t_end = (int)(((int64_t)(split + 1) * T) / ns);
   const int tiles_per_page = S / kTile;
+  auto phys_tile = [&](int v) { return v >= st ? v + shift : v; };
   const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
 
   if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
-    for (int idx = lane; idx < G * kCols; idx += 64) {
-      const int h = idx / kCols;
-      a.o_part[((row0 + h) * ns + split) * D + c0 + (idx - h * kCols)] = 0.f;
+    for (int idx = lane; idx < 16 * kCols; idx += 64) {
+      const int r = idx / kCols;
+      if (row_valid(r)) a.o_part[(out_row(r) * ns + split) * D + c0 + (idx - r * kCols)] = 0.f;
     }
-    if (wave == 0 && lane < G) a.lse_part[(row0 + lane) * ns + split] = -INFINITY;
+    if (wave == 0 && lane < 16 && row_valid(lane))
+      a.lse_part[out_row(lane) * ns + split] = -INFINITY;
     return;
   }
   const int t_last = t_end - 1;
 
-  // q group, B operand of the score MFMA: q[h = col][c0 + 32*j + 8*grp .. +8], zero for h >= G.
-  // Every lane loads (a clamped row) so no load sits under a divergent branch.
+  // q block, B operand of the score MFMA: row r = col, columns c0 + 32*j + 8*grp .. +8; zero for
+  // rows past the last query. Every lane loads (a clamped row) so no load sits under a divergent
+  // branch.
   bf16x8 qop[kKSteps];
   {
-    const uint16_t* qg = a.q + row0 * D;
-    const int hq = col < G ? col : G - 1;
+    const bool rv = row_valid(col);
+    const uint16_t* qr = a.q + out_row(rv ? col : col % G) * D;  // query qb * kQB is valid
 #pragma unroll
     for (int j = 0; j < kKSteps; ++j) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(qg + hq * D + c0 + 32 * j + 8 * grp);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qr + c0 + 32 * j + 8 * grp);
       const u32x4 z = {0u, 0u, 0u, 0u};
-      qop[j] = __builtin_bit_cast(bf16x8, col < G ? v : z);
+      qop[j] = __builtin_bit_cast(bf16x8, rv ? v : z);
     }
   }
 
@@ -194,16 +224,16 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   // never dereferenced: page 0 is read instead and the tile is masked.
   auto clamp_tile = [&](int ti) { return ti < t_end ? ti : t_last; };
   auto tile_base = [&](int ti, int phys, bool& ok) -> size_t {
-    const int tc = clamp_tile(ti);
+    const int tc = phys_tile(clamp_tile(ti));
     const bool page_ok = (unsigned)phys < (unsigned)a.num_pages;
     ok = ti < t_end && page_ok;
     const int pg = page_ok ? phys : 0;
     const int within = tc - (tc / tiles_per_page) * tiles_per_page;
     return (((size_t)pg * a.num_kv_heads + kvh) * S + within * kTile) * D;
   };
-  // Page ids of tiles t .. t+SUB-1 as a vector: lane u holds tile (t + u % SUB)'s id.
+  // Page ids of list entries t .. t+SUB-1 as a vector: lane u holds entry (t + u % SUB)'s id.
   auto load_page_ids = [&](int t) -> int32_t {
-    const int tc = clamp_tile(t + lane % SUB);
+    const int tc = phys_tile(clamp_tile(t + lane % SUB));
     return table_row[tc / tiles_per_page];
   };
 
@@ -212,7 +242,7 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   bool ok[SUB];
 #pragma unroll
   for (int u = 0; u < SUB; ++u) {
-    const int tc = clamp_tile(t_begin + u);
+    const int tc = phys_tile(clamp_tile(t_begin + u));
     base[u] = tile_base(t_begin + u, load_uniform(table_row, tc / tiles_per_page), ok[u]);
   }
   int32_t pid_next = load_page_ids(t_begin + SUB);
@@ -290,21 +320,23 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
     }
     buf ^= 1;
 
-    // Mask and online softmax for head `col` over the SUB*16 keys of the step.
-    int key_lo[SUB], key_hi[SUB];
+    // Mask and online softmax for row `col` over the SUB*16 keys of the step. Key t is attended
+    // by the row iff its page is valid, t < row_n and (t >= row_lo or t < sink); it is read at
+    // all (in_union) iff its page is valid, t < n and (t >= lo or t < sk).
+    int tok0[SUB];
     bool full = true;
     float mt = -INFINITY;
     float s2[SUB][4];
+    auto in_union = [&](int u, int t) { return ok[u] && t < n && (t >= lo || t < sk); };
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
-      const int tok0 = (t0 + u) * kTile;
-      key_lo[u] = ok[u] ? (lo > tok0 ? lo : tok0) : tok0;
-      key_hi[u] = ok[u] ? (n < tok0 + kTile ? n : tok0 + kTile) : tok0;
-      full = full && key_lo[u] == tok0 && key_hi[u] == tok0 + kTile;
+      tok0[u] = phys_tile(t0 + u) * kTile;
+      full = full && ok[u] && tok0[u] + kTile <= n && (tok0[u] >= lo || tok0[u] + kTile <= sk);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = tok0 + 4 * grp + i;
-        s2[u][i] = (t >= key_lo[u] && t < key_hi[u]) ? sc[u][i] * a.scale_log2 : -INFINITY;
+        const int t = tok0[u] + 4 * grp + i;
+        const bool att = ok[u] && t < row_n && (t >= row_lo || t < a.sink);
+        s2[u][i] = att ? sc[u][i] * a.scale_log2 : -INFINITY;
         mt = fmaxf(mt, s2[u][i]);
       }
     }
@@ -357,8 +389,7 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
       if (!full) {  // masked keys: V := 0 (their p is 0, but 0 * NaN would not be)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = (t0 + u) * kTile + 4 * grp + i;
-          const bool valid = t >= key_lo[u] && t < key_hi[u];
+          const bool valid = in_union(u, tok0[u] + 4 * grp + i);
 #pragma unroll
           for (int d = 0; d < Sh::kVDwords; ++d) vr[i][d] = valid ? vr[i][d] : 0u;
         }
@@ -393,14 +424,14 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
     pid_next = pid_after;
   }
 
-  // Normalise and write this wave's columns of the partial output; lane holds heads 4*grp + i.
+  // Normalise and write this wave's columns of the partial output; lane holds rows 4*grp + i.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * grp + i;
     const float lh = __shfl(l_run, h);
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
-    if (h < G) {
-      float* dst = a.o_part + ((row0 + h) * ns + split) * D + c0 + kVE * col;
+    if (row_valid(h)) {
+      float* dst = a.o_part + (out_row(h) * ns + split) * D + c0 + kVE * col;
 #pragma unroll
       for (int e4 = 0; e4 < kVE; e4 += 4) {
         const f32x4 v4 = {acc[e4][i] * inv, acc[e4 + 1][i] * inv, acc[e4 + 2][i] * inv,
@@ -409,16 +440,18 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
       }
     }
   }
-  if (wave == 0 && lane < G) {
+  if (wave == 0 && lane < 16 && row_valid(lane)) {
     const float lse = (m_run == -INFINITY) ? -INFINITY : (m_run + __log2f(l_run)) * kLn2;
-    a.lse_part[(row0 + lane) * ns + split] = lse;
+    a.lse_part[out_row(lane) * ns + split] = lse;
   }
 }
 
 template <int D, int G>
 hipError_t launch(const Stage1Args& args, bool shared, int batch, hipStream_t stream) {
   constexpr int kSub = DECODE_ATTN_STAGE1_SUB;
-  dim3 grid(args.num_splits, args.num_kv_heads, batch);
+  // Query blocks of one split are num_splits workgroups apart, so with a split count that is a
+  // multiple of 8 they land on the same XCD and share its L2 for the tiles they both read.
+  dim3 grid(args.num_splits * args.num_qblocks, args.num_kv_heads, batch);
   dim3 block(Shape<D>::kThreads);
   void* kargs[] = {const_cast<Stage1Args*>(&args)};
   const void* fn = shared ? reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, true>)

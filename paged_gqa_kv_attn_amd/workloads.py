@@ -120,7 +120,7 @@ def ragged_ctx_lens(rng: np.random.Generator, batch: int, low: int = 3800,
 @dataclasses.dataclass
 class LayerInputs:
     """Host arrays for one layer call."""
-    q: np.ndarray            # uint16 [B, Hq, D]
+    q: np.ndarray            # uint16 [B, Hq, D], or [B, L, Hq, D] for L > 1 query tokens
     k_pool: np.ndarray       # uint16 [P, Hkv, S, D]
     v_pool: np.ndarray       # uint16 [P, Hkv, S, D]
     block_table: np.ndarray  # int32  [B, max_pages_per_seq]
@@ -128,10 +128,12 @@ class LayerInputs:
     scale: float
     window: int
     page_size: int
+    sink: int = 0            # leading keys a sliding layer also attends
+    q_len: int = 1           # query tokens per sequence
 
     @property
     def dims(self):
-        B, Hq, D = self.q.shape
+        B, Hq, D = (self.q.shape[0],) + self.q.shape[-2:]
         P, Hkv, S, _ = self.k_pool.shape
         return dict(B=B, Hq=Hq, Hkv=Hkv, D=D, S=S, P=P, M=self.block_table.shape[1])
 
@@ -141,25 +143,36 @@ def attended_range(n: int, window: int) -> tuple[int, int]:
     return (max(0, n - window) if window > 0 else 0), n
 
 
+def attended_spans(n: int, window: int, sink: int = 0) -> list[tuple[int, int]]:
+    """Disjoint key spans a layer reads: [0, min(sink, lo)) for a sliding layer with sinks, then
+    [lo, n). Used only to decide which pages to allocate and poison."""
+    lo, hi = attended_range(n, window)
+    sk = min(sink, lo) if window > 0 else 0
+    return ([(0, sk)] if sk > 0 else []) + ([(lo, hi)] if hi > lo else [])
+
+
 def make_layer_inputs(ctx_lens: Sequence[int], num_q_heads: int, num_kv_heads: int, head_dim: int,
                       page_size: int = 16, window: int = 0, scale: Optional[float] = None,
                       num_pages: Optional[int] = None, pool_factor: int = 2, q_mult: float = 1.0,
                       seed=0, poison: bool = True, max_pages_per_seq: Optional[int] = None,
-                      value_dist: str = "normal") -> LayerInputs:
+                      value_dist: str = "normal", sink: int = 0,
+                      q_len: int = 1) -> LayerInputs:
     """Draw one layer's inputs. ``seed`` is anything ``np.random.SeedSequence`` accepts.
 
     Pages are allocated only for the logical pages holding attended keys; all other block-table
-    entries are -1. ``value_dist`` "normal" draws N(0,1) values, "zero" leaves them 0."""
+    entries are -1. ``value_dist`` "normal" draws N(0,1) values, "zero" leaves them 0. ``sink``
+    (sliding layers) also attends the first ``sink`` keys of each sequence. ``q_len`` > 1 draws
+    q as [B, L, Hq, D]: the last L cached keys are the new tokens, each query attending causally
+    (so a window reaches L - 1 keys further back for the first of them)."""
     ctx = np.asarray(ctx_lens, dtype=np.int32)
     B, S, D = len(ctx), int(page_size), int(head_dim)
     ss = np.random.SeedSequence(seed)
     rq, rk, rv, rp = (np.random.default_rng(s) for s in ss.spawn(4))
 
-    ranges = [attended_range(int(n), window) for n in ctx]
-    first = [lo // S for lo, n in ranges]
-    last = [(n - 1) // S if n > 0 else -1 for lo, n in ranges]
-    need = [max(0, l - f + 1) for f, l in zip(first, last)]
-    total = int(sum(need))
+    reach = window + q_len - 1 if window > 0 else 0
+    spans = [attended_spans(int(n), reach, sink) for n in ctx]
+    pages = [sorted({j for a, e in sp for j in range(a // S, (e - 1) // S + 1)}) for sp in spans]
+    total = int(sum(len(pg) for pg in pages))
     P = int(num_pages) if num_pages is not None else max(1, pool_factor * total)
     if P < total:
         raise ValueError("pool of %d pages cannot hold %d pages" % (P, total))
@@ -170,7 +183,7 @@ def make_layer_inputs(ctx_lens: Sequence[int], num_q_heads: int, num_kv_heads: i
     logical = []  # (b, logical page) for each allocated page, in allocation order
     cursor = 0
     for b in range(B):
-        for j in range(first[b], last[b] + 1):
+        for j in pages[b]:
             table[b, j] = perm[cursor]
             logical.append((b, j))
             cursor += 1
@@ -190,23 +203,25 @@ def make_layer_inputs(ctx_lens: Sequence[int], num_q_heads: int, num_kv_heads: i
         else:
             raise ValueError(value_dist)
         if poison:
-            # Slots of allocated pages outside [lo, n): before the window, after the last key.
+            # Slots of allocated pages holding no attended key: before the window (or between
+            # the sink keys and the window), after the last key.
             for (b, j), p in zip(logical, used):
-                lo, n = ranges[b]
-                a = max(0, lo - j * S)
-                e = min(S, n - j * S)
-                if a > 0:
-                    k_pool[p, :, :a] = BF16_QNAN
-                    v_pool[p, :, :a] = BF16_QNAN
-                if e < S:
-                    k_pool[p, :, e:] = BF16_QNAN
-                    v_pool[p, :, e:] = BF16_QNAN
+                t0 = j * S
+                if any(a <= t0 and t0 + S <= e for a, e in spans[b]):
+                    continue
+                t = np.arange(t0, t0 + S)
+                keep = np.zeros(S, dtype=bool)
+                for a, e in spans[b]:
+                    keep |= (t >= a) & (t < e)
+                k_pool[p, :, ~keep] = BF16_QNAN
+                v_pool[p, :, ~keep] = BF16_QNAN
 
-    q = f32_to_bf16_bits(np.float32(q_mult) *
-                         rq.standard_normal((B, num_q_heads, D), dtype=np.float32))
+    q_shape = (B, num_q_heads, D) if q_len == 1 else (B, q_len, num_q_heads, D)
+    q = f32_to_bf16_bits(np.float32(q_mult) * rq.standard_normal(q_shape, dtype=np.float32))
     return LayerInputs(q=q, k_pool=k_pool, v_pool=v_pool, block_table=table, ctx_lens=ctx,
                        scale=float(scale if scale is not None else 1.0 / math.sqrt(D)),
-                       window=int(window), page_size=S)
+                       window=int(window), page_size=S, sink=int(sink) if window > 0 else 0,
+                       q_len=int(q_len))
 
 
 def workload_ctx_lens(wl: Workload) -> np.ndarray:
@@ -216,40 +231,45 @@ def workload_ctx_lens(wl: Workload) -> np.ndarray:
     return np.asarray(wl.ctx, dtype=np.int32)
 
 
-def make_workload_layer(name: str, kind: str, poison: bool = True) -> LayerInputs:
-    """Inputs of layer ``kind`` ("global"/"sliding") of workload ``name``; seed = (index, kind)."""
+def make_workload_layer(name: str, kind: str, poison: bool = True, sink: int = 0,
+                        q_len: int = 1) -> LayerInputs:
+    """Inputs of layer ``kind`` ("global"/"sliding") of workload ``name``; seed = (index, kind),
+    extended by (sink, q_len) when either differs from the plain single-token layer."""
     wl = WORKLOADS[name]
     spec = wl.layers[kind]
     ctx = workload_ctx_lens(wl)
     seed = [wl.index, 0 if kind == "global" else 1]
+    if sink or q_len != 1:
+        seed += [sink, q_len]
     return make_layer_inputs(ctx, spec.num_q_heads, spec.num_kv_heads, spec.head_dim,
                              page_size=wl.page_size, window=spec.window, scale=spec.scale,
                              num_pages=wl.num_pages, pool_factor=wl.pool_factor, q_mult=spec.q_mult,
-                             seed=seed, poison=poison)
+                             seed=seed, poison=poison, sink=sink, q_len=q_len)
 
 
 def algorithmic_bytes(ctx_lens: Sequence[int], num_q_heads: int, num_kv_heads: int, head_dim: int,
-                      page_size: int = 16, window: int = 0, k_eq_v: bool = False) -> int:
-    """Bytes the method must move for one layer call: attended K and V (bf16; K only when the
-    values are the keys), q (bf16), out (fp32) and the block-table entries of the pages touched
-    (int32)."""
+                      page_size: int = 16, window: int = 0, k_eq_v: bool = False, sink: int = 0,
+                      q_len: int = 1) -> int:
+    """Bytes the method must move for one layer call: K and V (bf16; K only when the values are
+    the keys) of every key some query attends, each once, q (bf16), out (fp32) and the
+    block-table entries of the pages touched (int32)."""
+    reach = window + q_len - 1 if window > 0 else 0
     kv = 0
     table = 0
     for n in ctx_lens:
-        lo, hi = attended_range(int(n), window)
-        e = max(0, hi - lo)
-        kv += e * num_kv_heads * head_dim * 2 * (1 if k_eq_v else 2)
-        if e:
-            table += ((hi - 1) // page_size - lo // page_size + 1) * 4
-    B = len(ctx_lens)
-    return kv + B * num_q_heads * head_dim * 2 + B * num_q_heads * head_dim * 4 + table
+        spans = attended_spans(int(n), reach, sink)
+        kv += sum(e - a for a, e in spans) * num_kv_heads * head_dim * 2 * (1 if k_eq_v else 2)
+        pages = {j for a, e in spans for j in range(a // page_size, (e - 1) // page_size + 1)}
+        table += len(pages) * 4
+    rows = len(ctx_lens) * q_len * num_q_heads
+    return kv + rows * head_dim * 2 + rows * head_dim * 4 + table
 
 
 def algorithmic_flops(ctx_lens: Sequence[int], num_q_heads: int, head_dim: int,
-                      window: int = 0) -> int:
-    """4 * D * Hq flops per attended key (q.k and p.v, multiply and add)."""
+                      window: int = 0, sink: int = 0, q_len: int = 1) -> int:
+    """4 * D flops (q.k and p.v, multiply and add) per query head and key it attends."""
     total = 0
     for n in ctx_lens:
-        lo, hi = attended_range(int(n), window)
-        total += max(0, hi - lo)
+        for i in range(q_len):
+            total += sum(e - a for a, e in attended_spans(int(n) - q_len + 1 + i, window, sink))
     return 4 * head_dim * num_q_heads * total

@@ -50,21 +50,23 @@ def make_plan(inp: LayerInputs, **kw):
     args = dict(batch=d["B"], num_q_heads=d["Hq"], num_kv_heads=d["Hkv"], head_dim=d["D"],
                 page_size=d["S"], max_pages_per_seq=d["M"], num_pages=d["P"],
                 max_ctx_len=int(inp.ctx_lens.max()) if len(inp.ctx_lens) else 0,
-                window=inp.window)
+                window=inp.window, sink=inp.sink, q_len=inp.q_len)
     args.update(kw)
     return pda.decode_attn_plan(**args)
 
 
 def run(inp: LayerInputs, plan=None, dev_bufs=None, batch=None, **plan_kw):
-    """Run the layer on the GPU; returns (out [B,Hq,D] f32, lse [B,Hq] f32) as numpy."""
+    """Run the layer on the GPU; returns (out [B,Hq,D] f32, lse [B,Hq] f32) as numpy, with an
+    extra query axis after B ([B,L,Hq,D], [B,L,Hq]) when the inputs hold L > 1 queries."""
     import torch
     ensure_library()
     plan = plan or make_plan(inp, **plan_kw)
     t = dev_bufs or upload(inp)
     d = inp.dims
     B = d["B"] if batch is None else batch
-    out = torch.full((d["B"], d["Hq"], d["D"]), float("nan"), device=device())
-    lse = torch.full((d["B"], d["Hq"]), float("nan"), device=device())
+    lead = (d["B"],) if inp.q_len == 1 else (d["B"], inp.q_len)
+    out = torch.full(lead + (d["Hq"], d["D"]), float("nan"), device=device())
+    lse = torch.full(lead + (d["Hq"],), float("nan"), device=device())
     ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=device())
     if inp.window > 0:
         pda.decode_attn_sliding(plan, t["q"], t["k"], t["v"], t["bt"], t["ctx"], B, inp.window,
@@ -77,6 +79,12 @@ def run(inp: LayerInputs, plan=None, dev_bufs=None, batch=None, **plan_kw):
 
 
 def reference(inp: LayerInputs):
+    if inp.q_len > 1:
+        return oracle.decode_attn_multi(inp.q, inp.k_pool, inp.v_pool, inp.block_table,
+                                        inp.ctx_lens, inp.scale, inp.window, inp.sink)
+    if inp.sink > 0:
+        return oracle.decode_attn_sink(inp.q, inp.k_pool, inp.v_pool, inp.block_table,
+                                       inp.ctx_lens, inp.scale, inp.window, inp.sink)
     return oracle.decode_attn(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.ctx_lens,
                               inp.scale, window=inp.window)
 

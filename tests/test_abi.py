@@ -43,11 +43,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_plan_struct_layout_matches_header():
-    # 13 int32 problem fields, 4 int32, 2 uint64, uint32 magic, 7 int32 reserved (+ padding)
-    assert ctypes.sizeof(binding.Problem) == 52
-    assert binding.Plan.workspace_bytes.offset == 72
-    assert binding.Plan.magic.offset == 88
-    assert ctypes.sizeof(binding.Plan) == 120
+    # 15 int32 problem fields, 4 int32, 2 uint64, uint32 magic, 7 int32 reserved (+ padding)
+    assert ctypes.sizeof(binding.Problem) == 60
+    assert binding.Plan.workspace_bytes.offset == 80
+    assert binding.Plan.magic.offset == 96
+    assert ctypes.sizeof(binding.Plan) == 128
 
 
 def plan(**kw):
@@ -58,8 +58,8 @@ def plan(**kw):
     return binding.decode_attn_plan(**base)
 
 
-def expected_workspace(B, Hq, ns, D):
-    rows = B * Hq * ns
+def expected_workspace(B, Hq, ns, D, L=1):
+    rows = B * L * Hq * ns
     lse_off = -(-rows * D * 4 // 256) * 256
     return lse_off, -(-(lse_off + rows * 4) // 256) * 256
 
@@ -70,6 +70,13 @@ def expected_workspace(B, Hq, ns, D):
     (dict(batch=2, max_pages_per_seq=4160, num_pages=16384, max_ctx_len=66560), 64),
     (dict(batch=8, max_pages_per_seq=80, max_ctx_len=1280), 16),      # 16 pairs
     (dict(num_kv_heads=8, head_dim=256, window=1024), 16),            # 65 tiles, 32 pairs
+    (dict(num_kv_heads=8, head_dim=256, window=1024, sink=4), 16),    # + 1 sink tile
+    (dict(batch=1, num_kv_heads=8, head_dim=256, window=64, max_ctx_len=8192), 3),  # 5 tiles
+    (dict(batch=1, num_kv_heads=8, head_dim=256, window=64, max_ctx_len=8192, sink=40), 4),
+    (dict(q_len=4), 16),                                              # 2 query blocks of 2
+    (dict(q_len=2), 32),                                              # 1 block: as q_len 1
+    (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024,
+          q_len=8), 32),                                              # G 4: capped by tiles
     (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024), 32),
     (dict(batch=1, max_pages_per_seq=4, max_ctx_len=64), 2),          # capped: >= 2 tiles/split
 ])
@@ -79,7 +86,7 @@ def test_plan_split_counts(kw, splits):
     assert p.kind == (2 if p.problem.window else 1)
     assert p.group_size == p.problem.num_q_heads // p.problem.num_kv_heads
     off, total = expected_workspace(p.problem.batch, p.problem.num_q_heads, splits,
-                                    p.problem.head_dim)
+                                    p.problem.head_dim, p.problem.q_len)
     assert p.partial_lse_offset == off and p.workspace_bytes == total
     assert p.magic == binding.PLAN_MAGIC
 
@@ -98,7 +105,7 @@ def test_plan_values_are_keys_doubles_the_workgroups():
     assert plan(values_are_keys=True).num_splits == 64
     assert plan(batch=1, max_pages_per_seq=8256, num_pages=16384, max_ctx_len=132096,
                 values_are_keys=True).num_splits == 256
-    prob = binding.Problem(4, 16, 2, 512, 16, 2112, 16896, 33792, 0, 256, 0, 0, 2)
+    prob = binding.Problem(4, 16, 2, 512, 16, 2112, 16896, 33792, 0, 256, 0, 0, 2, 0, 0)
     out = binding.Plan()
     assert binding.load_library().decode_attn_plan(ctypes.byref(prob), ctypes.byref(out)) == \
         ERR_SHAPE
@@ -120,6 +127,10 @@ def test_plan_force_and_cap():
     (dict(batch=0), ERR_SHAPE),
     (dict(num_pages=0), ERR_SHAPE),
     (dict(window=-1), ERR_SHAPE),
+    (dict(window=64, sink=-1), ERR_SHAPE),
+    (dict(q_len=-1), ERR_SHAPE),
+    (dict(q_len=17), ERR_SHAPE),
+    (dict(batch=4096, q_len=16), ERR_SHAPE),     # 65536 (sequence, token) pairs
     (dict(force_splits=1025), ERR_SHAPE),
     (dict(max_splits=2000), ERR_SHAPE),
     (dict(head_dim=128), ERR_UNSUPPORTED),

@@ -308,6 +308,155 @@ def test_window_at_least_context_equals_global():
     np.testing.assert_array_equal(g[1], s[1])
 
 
+# ----------------------------------------------------------------------------- sink + window views
+
+
+@pytest.mark.parametrize("window,sink", [(1, 1), (16, 4), (17, 16), (32, 33), (5, 40)])
+def test_sink_window_bounds_with_counting_values(window, sink):
+    """scale 0: out = mean of V over exactly the attended keys [0, min(sink, n)) u [n - W, n);
+    V_t encodes t, so the mean pins both ranges (and that overlapping keys count once)."""
+    S, D = 16, 4
+    rng = np.random.default_rng(15)
+    for n in range(1, 81):
+        v = _count_values(n, D)
+        keys = [rand_bits(rng, (n, 1, D))]
+        kp, vp, table = paged(keys, [bf(v)], S, rng)
+        q = rand_bits(rng, (1, 1, D))
+        out, lse = oracle.decode_attn_sink(q, kp, vp, table, [n], 0.0, window, sink)
+        t = np.array(sorted(set(range(min(sink, n))) | set(range(max(0, n - window), n))))
+        expect = np.array([np.mean(t % 16), np.mean(t // 16), 1.0, -np.mean(t % 7)])
+        np.testing.assert_allclose(out[0, 0], expect, atol=1e-12,
+                                   err_msg="n=%d W=%d sink=%d" % (n, window, sink))
+        assert lse[0, 0] == pytest.approx(math.log(len(t)), abs=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_sink_window_equals_global_over_the_concatenated_view(seed):
+    """Attention over [0, sink) u [n - W, n) equals global attention over a new cache holding
+    exactly those keys, in order, on fresh pages: the view is a concatenation."""
+    rng = np.random.default_rng(40 + seed)
+    S, D, Hq, Hkv = 16, 32, 4, 2
+    ns = [int(x) for x in rng.integers(1, 140, size=3)]
+    window, sink = int(rng.integers(1, 60)), int(rng.integers(1, 40))
+    keys = [rand_bits(rng, (n, Hkv, D)) for n in ns]
+    vals = [rand_bits(rng, (n, Hkv, D)) for n in ns]
+    kp, vp, table = paged(keys, vals, S, rng)
+    q = rand_bits(rng, (len(ns), Hq, D))
+    out, lse = oracle.decode_attn_sink(q, kp, vp, table, ns, 0.3, window, sink)
+    kept = [sorted(set(range(min(sink, n))) | set(range(max(0, n - window), n))) for n in ns]
+    kp2, vp2, table2 = paged([k[idx] for k, idx in zip(keys, kept)],
+                             [v[idx] for v, idx in zip(vals, kept)], S, rng)
+    out2, lse2 = oracle.decode_attn(q, kp2, vp2, table2, [len(i) for i in kept], 0.3)
+    np.testing.assert_allclose(out, out2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse2, rtol=0, atol=1e-12)
+
+
+def test_sink_reduces_to_sliding_and_global():
+    """sink 0 is the sliding layer; window 0, or sink + window covering the context, is global."""
+    rng = np.random.default_rng(44)
+    S, D, Hq, Hkv = 16, 16, 2, 1
+    ns = [1, 31, 64, 99]
+    keys = [rand_bits(rng, (n, Hkv, D)) for n in ns]
+    vals = [rand_bits(rng, (n, Hkv, D)) for n in ns]
+    kp, vp, table = paged(keys, vals, S, rng)
+    q = rand_bits(rng, (len(ns), Hq, D))
+    glob = oracle.decode_attn(q, kp, vp, table, ns, 0.2)
+    slid = oracle.decode_attn(q, kp, vp, table, ns, 0.2, window=20)
+    for got, want in ((oracle.decode_attn_sink(q, kp, vp, table, ns, 0.2, 20, 0), slid),
+                      (oracle.decode_attn_sink(q, kp, vp, table, ns, 0.2, 0, 7), glob),
+                      (oracle.decode_attn_sink(q, kp, vp, table, ns, 0.2, 20, 80), glob)):
+        np.testing.assert_allclose(got[0], want[0], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(got[1], want[1], rtol=0, atol=1e-12)
+
+
+def test_sink_pages_outside_the_view_are_never_read():
+    """Pages holding no attended key may be invalid ids: they are not dereferenced."""
+    rng = np.random.default_rng(45)
+    S, D = 16, 8
+    n, window, sink = 100, 20, 10
+    keys = [rand_bits(rng, (n, 1, D))]
+    vals = [rand_bits(rng, (n, 1, D))]
+    kp, vp, table = paged(keys, vals, S, rng)
+    q = rand_bits(rng, (1, 1, D))
+    want = oracle.decode_attn_sink(q, kp, vp, table, [n], 0.5, window, sink)
+    table[0, 1:5] = -1  # keys 16..79: neither sink nor window
+    got = oracle.decode_attn_sink(q, kp, vp, table, [n], 0.5, window, sink)
+    assert np.array_equal(got[0], want[0]) and np.array_equal(got[1], want[1])
+
+
+# ----------------------------------------------------------------------------- multi-token decode
+
+
+@pytest.mark.parametrize("L,window,sink", [(2, 0, 0), (3, 0, 0), (4, 17, 0), (7, 16, 4),
+                                           (5, 1, 0), (8, 33, 40)])
+def test_multi_token_bounds_with_counting_values(L, window, sink):
+    """scale 0: each query's output is the mean of V over exactly its key set, whose upper end
+    moves with the query (t <= n - L + i) and whose window moves with it."""
+    S, D = 16, 4
+    rng = np.random.default_rng(60 + L)
+    for n in range(1, 75):
+        v = _count_values(n, D)
+        kp, vp, table = paged([rand_bits(rng, (n, 1, D))], [bf(v)], S, rng)
+        q = rand_bits(rng, (1, L, 1, D))
+        out, lse = oracle.decode_attn_multi(q, kp, vp, table, [n], 0.0, window, sink)
+        for i in range(L):
+            p = n - L + i
+            if p < 0:
+                assert np.all(out[0, i, 0] == 0) and lse[0, i, 0] == -np.inf
+                continue
+            lo = max(0, p + 1 - window) if window else 0
+            sk = min(sink, lo) if window else 0
+            t = np.array(list(range(sk)) + list(range(lo, p + 1)))
+            expect = np.array([np.mean(t % 16), np.mean(t // 16), 1.0, -np.mean(t % 7)])
+            np.testing.assert_allclose(out[0, i, 0], expect, atol=1e-12,
+                                       err_msg="n=%d L=%d i=%d" % (n, L, i))
+            assert lse[0, i, 0] == pytest.approx(math.log(len(t)), abs=1e-13)
+
+
+@pytest.mark.parametrize("G,L,window", [(1, 2, 0), (2, 4, 0), (4, 3, 9), (8, 2, 0), (2, 8, 20)])
+def test_multi_token_equals_masked_sdpa(G, L, window):
+    """Against torch's scaled_dot_product_attention in fp64 on the dense keys with an explicit
+    causal (and window) mask: the prefill-style formulation of the same queries."""
+    import torch
+    rng = np.random.default_rng(70 + G + L)
+    S, D, Hkv = 16, 32, 2
+    Hq = G * Hkv
+    ns = [L, 17, 50, 97]
+    keys = [rand_bits(rng, (n, Hkv, D)) for n in ns]
+    vals = [rand_bits(rng, (n, Hkv, D)) for n in ns]
+    kp, vp, table = paged(keys, vals, S, rng)
+    q = rand_bits(rng, (len(ns), L, Hq, D))
+    scale = 0.2
+    out, lse = oracle.decode_attn_multi(q, kp, vp, table, ns, scale, window)
+    for b, n in enumerate(ns):
+        qt = torch.from_numpy(f64(q[b])).permute(1, 0, 2)                    # [Hq, L, D]
+        kt = torch.from_numpy(f64(keys[b])).permute(1, 0, 2).repeat_interleave(G, 0)
+        vt = torch.from_numpy(f64(vals[b])).permute(1, 0, 2).repeat_interleave(G, 0)
+        pos = torch.arange(n - L, n)[:, None]
+        t = torch.arange(n)[None, :]
+        mask = (t <= pos) & ((t > pos - window) if window else True)
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                                               scale=scale)
+        np.testing.assert_allclose(out[b], ref.permute(1, 0, 2).numpy(), rtol=0, atol=1e-12)
+        s = scale * (qt @ kt.transpose(1, 2))
+        ref_lse = torch.logsumexp(s.masked_fill(~mask, -np.inf), dim=-1).T.numpy()
+        np.testing.assert_allclose(lse[b], ref_lse, rtol=0, atol=1e-12)
+
+
+def test_multi_token_one_query_is_single_token_decode():
+    rng = np.random.default_rng(80)
+    S, D, Hq, Hkv = 16, 16, 4, 2
+    ns = [1, 31, 64, 99]
+    keys = [rand_bits(rng, (n, Hkv, D)) for n in ns]
+    vals = [rand_bits(rng, (n, Hkv, D)) for n in ns]
+    kp, vp, table = paged(keys, vals, S, rng)
+    q = rand_bits(rng, (len(ns), 1, Hq, D))
+    for window, sink in ((0, 0), (20, 0), (20, 6)):
+        got = oracle.decode_attn_multi(q, kp, vp, table, ns, 0.3, window, sink)
+        want = oracle.decode_attn_sink(q[:, 0], kp, vp, table, ns, 0.3, window, sink)
+        assert np.array_equal(got[0][:, 0], want[0]) and np.array_equal(got[1][:, 0], want[1])
+
+
 def test_empty_context_gives_zero_and_minus_inf():
     inp = make_layer_inputs([0, 3], 2, 1, 16, page_size=16, seed=15)
     out, lse = oracle.decode_attn(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.ctx_lens,
