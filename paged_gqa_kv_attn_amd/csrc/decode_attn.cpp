@@ -1,7 +1,7 @@
 // decode_attn.cpp — the extern "C" entry points of libdecode_attn.so: planning, host-side argument
 // checks and the two kernel launches. Declared and documented in include/decode_attn.h.
 
-#include "../../include/decode_attn.h"
+#include "decode_attn.h"
 
 #include <hip/hip_runtime_api.h>
 

@@ -122,7 +122,9 @@ struct StepRegs {
 // SHARED: the pools are one buffer (layers whose values are their keys). Each tile is then read
 // once; every wave parks its K slice in LDS (rows padded by 16 bytes against bank conflicts) and
 // reads it back in the V operand layout.
-template <int D, int G, int SUB, bool SHARED>
+// GENERAL: several query tokens per sequence and/or sink keys. Without it (one query token, no
+// sinks) the row bounds are uniform and the query-block and sink arithmetic folds away.
+template <int D, int G, int SUB, bool SHARED, bool GENERAL>
 __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1Args a) {
   using Sh = Shape<D>;
   constexpr int kWaves = Sh::kWaves;
@@ -134,8 +136,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[SHARED ? kWaves : 1][SUB][16][kKvRow];
 
   const int ns = a.num_splits;
-  const int split = blockIdx.x % ns;
-  const int qb = blockIdx.x / ns;  // query block: queries [qb * kQB, qb * kQB + kQB)
+  const int split = GENERAL ? (int)blockIdx.x % ns : (int)blockIdx.x;
+  const int qb = GENERAL ? (int)blockIdx.x / ns : 0;  // query block: queries qb * kQB + [0, kQB)
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
   const int lane = threadIdx.x & 63;
@@ -146,7 +148,8 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   constexpr int kCols = Sh::kCols;
   using VRow = typename Sh::VRow;
   const int c0 = wave * kCols;  // first head-dim column of this wave
-  const int L = a.q_len;
+  const int L = GENERAL ? a.q_len : 1;
+  const int sink = GENERAL ? a.sink : 0;
 
   // The 16 MFMA rows: row r is query qb * kQB + r / G of the sequence, head kvh * G + r % G.
   // Output row index (b, query, head) in the [B, L, Hq] order of q and of the partials.
@@ -173,10 +176,10 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   const int q_last = (qb + 1) * kQB < L ? (qb + 1) * kQB - 1 : L - 1;
   const int n = query_end(q_last);
   const int lo = window_lo(query_end(qb * kQB));
-  const int sk = a.sink < lo ? a.sink : lo;
+  const int sk = sink < lo ? sink : lo;
   // This lane's row (scores and softmax use row = col).
-  const int row_n = row_valid(col) ? query_end(row_query(col)) : 0;
-  const int row_lo = window_lo(row_n);
+  const int row_n = GENERAL ? (row_valid(col) ? query_end(row_query(col)) : 0) : n;
+  const int row_lo = GENERAL ? window_lo(row_n) : lo;
   const int st = (sk + kTile - 1) / kTile;
   const int w0 = st > lo / kTile ? st : lo / kTile;
   const int tile_hi = (n + kTile - 1) / kTile;
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   const int t_begin = (int)(((int64_t)split * T) / ns);
   const int t_end = (int)(((int64_t)(split + 1) * T) / ns);
   const int tiles_per_page = S / kTile;
-  auto phys_tile = [&](int v) { return v >= st ? v + shift : v; };
+  auto phys_tile = [&](int v) { return (!GENERAL || v >= st) ? v + shift : v; };
   const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
 
   if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
@@ -322,20 +325,29 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
 
     // Mask and online softmax for row `col` over the SUB*16 keys of the step. Key t is attended
     // by the row iff its page is valid, t < row_n and (t >= row_lo or t < sink); it is read at
-    // all (in_union) iff its page is valid, t < n and (t >= lo or t < sk).
-    int tok0[SUB];
+    // all (in_union) iff its page is valid, t < n and (t >= lo or t < sk). The per-lane tests
+    // combine with & and | (no short circuit, hence no branches on the exec mask).
+    // Without GENERAL every row has the same bounds, folded per tile into one uniform range
+    // [klo, khi) (empty for an invalid page).
+    int tok0[SUB], klo[SUB], khi[SUB];
     bool full = true;
     float mt = -INFINITY;
     float s2[SUB][4];
-    auto in_union = [&](int u, int t) { return ok[u] && t < n && (t >= lo || t < sk); };
+    auto in_union = [&](int u, int t) {
+      if constexpr (GENERAL) return ok[u] & (t < n) & ((t >= lo) | (t < sk));
+      else return (t >= klo[u]) & (t < khi[u]);
+    };
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       tok0[u] = phys_tile(t0 + u) * kTile;
+      klo[u] = ok[u] ? (lo > tok0[u] ? lo : tok0[u]) : tok0[u] + kTile;
+      khi[u] = n < tok0[u] + kTile ? n : tok0[u] + kTile;
       full = full && ok[u] && tok0[u] + kTile <= n && (tok0[u] >= lo || tok0[u] + kTile <= sk);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = tok0[u] + 4 * grp + i;
-        const bool att = ok[u] && t < row_n && (t >= row_lo || t < a.sink);
+        const bool att = GENERAL ? ok[u] & (t < row_n) & ((t >= row_lo) | (t < sink))
+                                 : in_union(u, t);
         s2[u][i] = att ? sc[u][i] * a.scale_log2 : -INFINITY;
         mt = fmaxf(mt, s2[u][i]);
       }
@@ -446,16 +458,22 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   }
 }
 
+template <int D, int G, bool SHARED>
+const void* kernel_for(bool general) {
+  constexpr int kSub = DECODE_ATTN_STAGE1_SUB;
+  return general ? reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, SHARED, true>)
+                 : reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, SHARED, false>);
+}
+
 template <int D, int G>
 hipError_t launch(const Stage1Args& args, bool shared, int batch, hipStream_t stream) {
-  constexpr int kSub = DECODE_ATTN_STAGE1_SUB;
   // Query blocks of one split are num_splits workgroups apart, so with a split count that is a
   // multiple of 8 they land on the same XCD and share its L2 for the tiles they both read.
   dim3 grid(args.num_splits * args.num_qblocks, args.num_kv_heads, batch);
   dim3 block(Shape<D>::kThreads);
   void* kargs[] = {const_cast<Stage1Args*>(&args)};
-  const void* fn = shared ? reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, true>)
-                          : reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, false>);
+  const bool general = args.q_len > 1 || args.sink > 0;
+  const void* fn = shared ? kernel_for<D, G, true>(general) : kernel_for<D, G, false>(general);
   return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
 }
 
