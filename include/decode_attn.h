@@ -134,8 +134,8 @@ typedef struct {
  * Checks the problem, picks the split count and computes the workspace size.
  * Split rule: with T = ceil(e / 16) (+ 1 for a sliding window, whose edge may straddle a tile,
  * + ceil(sink / 16) for its sink keys) tiles of 16 keys for the longest range one query block
- * walks, e = min(max_ctx_len, W + min(L, 16 / G) - 1 or unlimited),
- * pairs = batch * Hkv * ceil(L / (16 / G)) and target = num_cus workgroups for head_dim 512 with
+ * walks, e = min(max_ctx_len, W + min(L, Q) - 1 or unlimited), with Q the queries of a block,
+ * pairs = batch * Hkv * ceil(L / Q) and target = num_cus workgroups for head_dim 512 with
  * separate pools (2 * num_cus for head_dim 256 or when values are keys),
  *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, ceil(T / 2)))
  * so every chunk holds at least 2 tiles (32 keys, one stage-1 loop step) when the context
@@ -174,7 +174,8 @@ int decode_attn_sliding(const decode_attn_plan_t* plan, const void* q, const voi
  * Writes the workspace, which holds two planes:
  *     o_part [B, L, Hq, num_splits, D] fp32 at byte offset 0
  *     lse    [B, L, Hq, num_splits]    fp32 at byte offset plan->partial_lse_offset
- * The queries of a sequence are taken in blocks of 16 / G (one block when L = 1). Split s of a
+ * The queries of a sequence are taken in blocks of 16 / G, or 32 / G when G * L > 16 (one
+ * block when L = 1). Split s of a
  * block covers the tiles [floor(s*T/ns), floor((s+1)*T/ns)) of the block's list of T 16-key
  * tiles (ns = num_splits). With lo and n those of the block's first and last query respectively,
  * the list holds the tiles 0 .. ceil(k/16) - 1 that overlap the sink keys [0, k), k = min(sink,

@@ -41,10 +41,9 @@ uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
 // Query tokens per sequence of a resolved problem (0 means 1).
 int q_len_of(const decode_attn_problem& p) { return p.q_len > 1 ? p.q_len : 1; }
 
-// Query blocks per (sequence, kv head): the 16 MFMA rows hold 16 / G queries of G heads each.
+// Query blocks per (sequence, kv head): a stage-1 workgroup serves 16 or 32 rows of G heads.
 int qblocks_of(const decode_attn_problem& p, int group_size) {
-  const int per_block = 16 / group_size;
-  return (q_len_of(p) + per_block - 1) / per_block;
+  return stage1_query_blocks(group_size, q_len_of(p));
 }
 
 // Workspace layout: o_part [B, L, Hq, ns, D] fp32, then (256-byte aligned) lse [B, L, Hq, ns]
@@ -205,10 +204,11 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   if (p.q_len == 0) p.q_len = 1;
 
   // Longest key range one workgroup walks, in 16-key tiles (a window may straddle one more;
-  // sink keys add their own tiles; the queries of a block widen a window by up to 16 / G - 1).
+  // sink keys add their own tiles; the queries of a block widen a window by their count - 1).
   const int64_t max_keys = (int64_t)p.max_pages_per_seq * p.page_size;
   int64_t e = p.max_ctx_len > 0 ? (p.max_ctx_len < max_keys ? p.max_ctx_len : max_keys) : max_keys;
-  const int64_t span = (int64_t)p.window + (p.q_len < 16 / G ? p.q_len : 16 / G) - 1;
+  const int per_block = stage1_block_queries(G, p.q_len);
+  const int64_t span = (int64_t)p.window + (p.q_len < per_block ? p.q_len : per_block) - 1;
   if (p.window > 0 && e > span) e = span;
   int64_t tiles = (e + kTile - 1) / kTile + (p.window > 0 ? 1 : 0);
   if (p.window > 0) tiles += ((int64_t)(p.sink < max_keys ? p.sink : max_keys) + kTile - 1) / kTile;

@@ -73,4 +73,19 @@ hipError_t launch_append(const AppendArgs& args, int batch, hipStream_t stream);
 // True when a stage-1 kernel is compiled for (head_dim, group_size).
 bool stage1_supported(int head_dim, int group_size);
 
+// Groups of 16 MFMA rows a stage-1 workgroup uses: two when the G * q_len rows of a sequence's
+// queries do not fit in 16 (then 32 / G queries share each tile read), else one.
+inline int stage1_row_groups(int group_size, int q_len) {
+  return (q_len > 1 && group_size * q_len > 16) ? 2 : 1;
+}
+
+// Queries one stage-1 workgroup serves, and the query blocks of one (sequence, kv head).
+inline int stage1_block_queries(int group_size, int q_len) {
+  return 16 * stage1_row_groups(group_size, q_len) / group_size;
+}
+inline int stage1_query_blocks(int group_size, int q_len) {
+  const int per = stage1_block_queries(group_size, q_len);
+  return (q_len + per - 1) / per;
+}
+
 }  // namespace decode_attn

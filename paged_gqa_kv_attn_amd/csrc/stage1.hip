@@ -98,11 +98,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-template <int D>
+#ifndef DECODE_ATTN_COLS_PER_WAVE_RG2
+#define DECODE_ATTN_COLS_PER_WAVE_RG2 128
+#endif
+
+// Columns per wave. Two row groups double the accumulators; 64 columns per wave (twice the
+// waves) keeps two waves per SIMD, but on MI355X it measured no faster than 128 with one.
+template <int D, int RG>
 struct Shape {
   static_assert(D == 256 || D == 512, "head_dim");
-  static constexpr int kCols = D == 512 ? DECODE_ATTN_COLS_PER_WAVE_512
-                                        : DECODE_ATTN_COLS_PER_WAVE_256;  // columns per wave
+  static constexpr int kCols =
+      RG == 2 ? (D == 512 ? DECODE_ATTN_COLS_PER_WAVE_RG2 : DECODE_ATTN_COLS_PER_WAVE_256)
+              : (D == 512 ? DECODE_ATTN_COLS_PER_WAVE_512 : DECODE_ATTN_COLS_PER_WAVE_256);
   static_assert(kCols == 64 || kCols == 128, "columns per wave");
   static constexpr int kWaves = D / kCols;
   static constexpr int kThreads = 64 * kWaves;
@@ -113,10 +120,10 @@ struct Shape {
 };
 
 // One step's worth of this wave's slice of K and V: SUB tiles of 16 keys.
-template <int D, int SUB>
+template <int D, int RG, int SUB>
 struct StepRegs {
-  bf16x8 k[SUB][Shape<D>::kKSteps];
-  typename Shape<D>::VRow v[SUB][4];  // tile u, keys 4*(lane/16)+i, i = 0..3
+  bf16x8 k[SUB][Shape<D, RG>::kKSteps];
+  typename Shape<D, RG>::VRow v[SUB][4];  // tile u, keys 4*(lane/16)+i, i = 0..3
 };
 
 // SHARED: the pools are one buffer (layers whose values are their keys). Each tile is then read
@@ -124,14 +131,17 @@ struct StepRegs {
 // reads it back in the V operand layout.
 // GENERAL: several query tokens per sequence and/or sink keys. Without it (one query token, no
 // sinks) the row bounds are uniform and the query-block and sink arithmetic folds away.
-template <int D, int G, int SUB, bool SHARED, bool GENERAL>
-__global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1Args a) {
-  using Sh = Shape<D>;
+// RG: groups of 16 MFMA rows per workgroup (2 only with GENERAL): 16 * RG rows share every tile
+// read, so up to 32 / G query tokens cost one pass over the keys.
+template <int D, int G, int SUB, bool SHARED, bool GENERAL, int RG>
+__global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const Stage1Args a) {
+  using Sh = Shape<D, RG>;
   constexpr int kWaves = Sh::kWaves;
   constexpr int kKSteps = Sh::kKSteps;
   constexpr int kVE = Sh::kVE;
+  static_assert(RG == 1 || (RG == 2 && GENERAL), "row groups");
 
-  __shared__ __attribute__((aligned(16))) f32x4 score_lds[2][SUB][kWaves][64];
+  __shared__ __attribute__((aligned(16))) f32x4 score_lds[2][SUB][RG][kWaves][64];
   constexpr int kKvRow = Sh::kCols + 8;  // padded row of a parked K slice (bf16 elements)
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[SHARED ? kWaves : 1][SUB][16][kKvRow];
 
@@ -151,9 +161,10 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   const int L = GENERAL ? a.q_len : 1;
   const int sink = GENERAL ? a.sink : 0;
 
-  // The 16 MFMA rows: row r is query qb * kQB + r / G of the sequence, head kvh * G + r % G.
-  // Output row index (b, query, head) in the [B, L, Hq] order of q and of the partials.
-  constexpr int kQB = 16 / G;
+  // The 16 * RG MFMA rows: row r is query qb * kQB + r / G of the sequence, head kvh * G + r % G
+  // (row group r / 16). Output row index (b, query, head) in the [B, L, Hq] order of q and of
+  // the partials.
+  constexpr int kQB = 16 * RG / G;
   auto row_query = [&](int r) { return qb * kQB + r / G; };
   auto row_valid = [&](int r) { return row_query(r) < L; };
   auto out_row = [&](int r) -> size_t {
@@ -177,9 +188,14 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   const int n = query_end(q_last);
   const int lo = window_lo(query_end(qb * kQB));
   const int sk = sink < lo ? sink : lo;
-  // This lane's row (scores and softmax use row = col).
-  const int row_n = GENERAL ? (row_valid(col) ? query_end(row_query(col)) : 0) : n;
-  const int row_lo = GENERAL ? window_lo(row_n) : lo;
+  // This lane's rows (scores and softmax use row 16 * rg + col in row group rg).
+  int row_n[RG], row_lo[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int rr = 16 * rg + col;
+    row_n[rg] = GENERAL ? (row_valid(rr) ? query_end(row_query(rr)) : 0) : n;
+    row_lo[rg] = GENERAL ? window_lo(row_n[rg]) : lo;
+  }
   const int st = (sk + kTile - 1) / kTile;
   const int w0 = st > lo / kTile ? st : lo / kTile;
   const int tile_hi = (n + kTile - 1) / kTile;
@@ -192,28 +208,30 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
 
   if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
-    for (int idx = lane; idx < 16 * kCols; idx += 64) {
+    for (int idx = lane; idx < 16 * RG * kCols; idx += 64) {
       const int r = idx / kCols;
       if (row_valid(r)) a.o_part[(out_row(r) * ns + split) * D + c0 + (idx - r * kCols)] = 0.f;
     }
-    if (wave == 0 && lane < 16 && row_valid(lane))
+    if (wave == 0 && lane < 16 * RG && row_valid(lane))
       a.lse_part[out_row(lane) * ns + split] = -INFINITY;
     return;
   }
   const int t_last = t_end - 1;
 
-  // q block, B operand of the score MFMA: row r = col, columns c0 + 32*j + 8*grp .. +8; zero for
-  // rows past the last query. Every lane loads (a clamped row) so no load sits under a divergent
-  // branch.
-  bf16x8 qop[kKSteps];
-  {
-    const bool rv = row_valid(col);
-    const uint16_t* qr = a.q + out_row(rv ? col : col % G) * D;  // query qb * kQB is valid
+  // q block, B operand of the score MFMA of row group rg: row 16 * rg + col, columns
+  // c0 + 32*j + 8*grp .. +8; zero for rows past the last query. Every lane loads (a clamped row)
+  // so no load sits under a divergent branch.
+  bf16x8 qop[RG][kKSteps];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int rr = 16 * rg + col;
+    const bool rv = row_valid(rr);
+    const uint16_t* qr = a.q + out_row(rv ? rr : col % G) * D;  // query qb * kQB is valid
 #pragma unroll
     for (int j = 0; j < kKSteps; ++j) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(qr + c0 + 32 * j + 8 * grp);
       const u32x4 z = {0u, 0u, 0u, 0u};
-      qop[j] = __builtin_bit_cast(bf16x8, rv ? v : z);
+      qop[rg][j] = __builtin_bit_cast(bf16x8, rv ? v : z);
     }
   }
 
@@ -240,7 +258,7 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
     return table_row[tc / tiles_per_page];
   };
 
-  StepRegs<D, SUB> r;
+  StepRegs<D, RG, SUB> r;
   size_t base[SUB];
   bool ok[SUB];
 #pragma unroll
@@ -266,25 +284,34 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
   // prefetch into a load at the top of every step.
   __asm__ volatile("; stage-1 prologue loads issued" ::: "memory");
 
-  float m_run = -INFINITY;  // running max (base-2 units) of head `col`
-  float l_run = 0.f;        // running sum of exp2(s - m_run) of head `col`
-  f32x4 acc[kVE];           // O[head 4*grp + i][column c0 + kVE*col + e] = acc[e][i]
+  float m_run[RG];   // running max (base-2 units) of row 16 * rg + col
+  float l_run[RG];   // running sum of exp2(s - m_run) of that row
+  f32x4 acc[RG][kVE];  // O[row 16 * rg + 4*grp + i][column c0 + kVE*col + e] = acc[rg][e][i]
 #pragma unroll
-  for (int e = 0; e < kVE; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rg = 0; rg < RG; ++rg) {
+    m_run[rg] = -INFINITY;
+    l_run[rg] = 0.f;
+#pragma unroll
+    for (int e = 0; e < kVE; ++e) acc[rg][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += SUB) {
     // Partial scores of this wave's columns for the SUB tiles of the step.
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
-      f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < kKSteps; j += 2) {
-        p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[u][j], qop[j], p0, 0, 0, 0);
-        if (j + 1 < kKSteps)
-          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[u][j + 1], qop[j + 1], p1, 0, 0, 0);
+      for (int rg = 0; rg < RG; ++rg) {
+        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < kKSteps; j += 2) {
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[u][j], qop[rg][j], p0, 0, 0, 0);
+          if (j + 1 < kKSteps)
+            p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[u][j + 1], qop[rg][j + 1], p1, 0, 0,
+                                                         0);
+        }
+        score_lds[buf][u][rg][wave][lane] = p0 + p1;
       }
-      score_lds[buf][u][wave][lane] = p0 + p1;
       if constexpr (SHARED) {
         // Park this wave's K slice of tile u (row col, columns 32j + 8grp) before the registers
         // are refilled; P.V reads it back as V.
@@ -314,25 +341,25 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
     __builtin_amdgcn_sched_barrier(0);
 
     lds_barrier();
-    f32x4 sc[SUB];
+    f32x4 sc[SUB][RG];
 #pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-      sc[u] = score_lds[buf][u][0][lane];
+    for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) sc[u] += score_lds[buf][u][w][lane];
-    }
+      for (int rg = 0; rg < RG; ++rg) {
+        sc[u][rg] = score_lds[buf][u][rg][0][lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) sc[u][rg] += score_lds[buf][u][rg][w][lane];
+      }
     buf ^= 1;
 
-    // Mask and online softmax for row `col` over the SUB*16 keys of the step. Key t is attended
-    // by the row iff its page is valid, t < row_n and (t >= row_lo or t < sink); it is read at
-    // all (in_union) iff its page is valid, t < n and (t >= lo or t < sk). The per-lane tests
-    // combine with & and | (no short circuit, hence no branches on the exec mask).
+    // Mask and online softmax for row 16 * rg + col over the SUB*16 keys of the step. Key t is
+    // attended by the row iff its page is valid, t < row_n and (t >= row_lo or t < sink); it is
+    // read at all (in_union) iff its page is valid, t < n and (t >= lo or t < sk). The per-lane
+    // tests combine with & and | (no short circuit, hence no branches on the exec mask).
     // Without GENERAL every row has the same bounds, folded per tile into one uniform range
     // [klo, khi) (empty for an invalid page).
     int tok0[SUB], klo[SUB], khi[SUB];
     bool full = true;
-    float mt = -INFINITY;
-    float s2[SUB][4];
     auto in_union = [&](int u, int t) {
       if constexpr (GENERAL) return ok[u] & (t < n) & ((t >= lo) | (t < sk));
       else return (t >= klo[u]) & (t < khi[u]);
@@ -343,46 +370,54 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
       klo[u] = ok[u] ? (lo > tok0[u] ? lo : tok0[u]) : tok0[u] + kTile;
       khi[u] = n < tok0[u] + kTile ? n : tok0[u] + kTile;
       full = full && ok[u] && tok0[u] + kTile <= n && (tok0[u] >= lo || tok0[u] + kTile <= sk);
+    }
+    i16x4 pop[SUB][RG];
+    float alpha[RG];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tok0[u] + 4 * grp + i;
-        const bool att = GENERAL ? ok[u] & (t < row_n) & ((t >= row_lo) | (t < sink))
-                                 : in_union(u, t);
-        s2[u][i] = att ? sc[u][i] * a.scale_log2 : -INFINITY;
-        mt = fmaxf(mt, s2[u][i]);
+    for (int rg = 0; rg < RG; ++rg) {
+      float mt = -INFINITY;
+      float s2[SUB][4];
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = tok0[u] + 4 * grp + i;
+          const bool att =
+              GENERAL ? ok[u] & (t < row_n[rg]) & ((t >= row_lo[rg]) | (t < sink)) : in_union(u, t);
+          s2[u][i] = att ? sc[u][rg][i] * a.scale_log2 : -INFINITY;
+          mt = fmaxf(mt, s2[u][i]);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float m_new = fmaxf(m_run[rg], mt);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      alpha[rg] = __builtin_amdgcn_exp2f(m_run[rg] - m_use);
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        float p[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s2[u][i] - m_use);
+        ps += (p[0] + p[1]) + (p[2] + p[3]);
+        // P as the A operand: P[row 16 * rg + col][keys 4*grp .. +3 of tile u] in bf16.
+        const u32x2 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+        pop[u][rg] = __builtin_bit_cast(i16x4, pa);
       }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float ps = 0.f;
-    i16x4 pop[SUB];
-#pragma unroll
-    for (int u = 0; u < SUB; ++u) {
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(s2[u][i] - m_use);
-      ps += (p[0] + p[1]) + (p[2] + p[3]);
-      // P as the A operand: P[head col][keys 4*grp .. +3 of tile u] in bf16.
-      const u32x2 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-      pop[u] = __builtin_bit_cast(i16x4, pa);
-    }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      l_run[rg] = l_run[rg] * alpha[rg] + ps;
+      m_run[rg] = m_new;
 
-    // Rescale the accumulator rows (heads 4*grp + i) when some running max moved.
-    if (__any(alpha != 1.f)) {
-      float al[4];
+      // Rescale the accumulator rows (16 * rg + 4*grp + i) when some running max moved.
+      if (__any(alpha[rg] != 1.f)) {
+        float al[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha[rg], 4 * grp + i);
 #pragma unroll
-      for (int e = 0; e < kVE; ++e)
+        for (int e = 0; e < kVE; ++e)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[e][i] *= al[i];
+          for (int i = 0; i < 4; ++i) acc[rg][e][i] *= al[i];
+      }
     }
 
     // P.V, one tile at a time.
@@ -413,10 +448,13 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
                           __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x05040100u)};
         const u32x2 bo = {__builtin_amdgcn_perm(vr[1][d], vr[0][d], 0x07060302u),
                           __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x07060302u)};
-        acc[2 * d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            pop[u], __builtin_bit_cast(i16x4, be), acc[2 * d], 0, 0, 0);
-        acc[2 * d + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-            pop[u], __builtin_bit_cast(i16x4, bo), acc[2 * d + 1], 0, 0, 0);
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+          acc[rg][2 * d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              pop[u][rg], __builtin_bit_cast(i16x4, be), acc[rg][2 * d], 0, 0, 0);
+          acc[rg][2 * d + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              pop[u][rg], __builtin_bit_cast(i16x4, bo), acc[rg][2 * d + 1], 0, 0, 0);
+        }
       }
     }
 
@@ -436,33 +474,44 @@ __global__ __launch_bounds__(Shape<D>::kThreads) void stage1_kernel(const Stage1
     pid_next = pid_after;
   }
 
-  // Normalise and write this wave's columns of the partial output; lane holds rows 4*grp + i.
+  // Normalise and write this wave's columns of the partial output; lane holds rows
+  // 16 * rg + 4*grp + i.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * grp + i;
-    const float lh = __shfl(l_run, h);
-    const float inv = lh > 0.f ? 1.f / lh : 0.f;
-    if (row_valid(h)) {
-      float* dst = a.o_part + (out_row(h) * ns + split) * D + c0 + kVE * col;
+  for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-      for (int e4 = 0; e4 < kVE; e4 += 4) {
-        const f32x4 v4 = {acc[e4][i] * inv, acc[e4 + 1][i] * inv, acc[e4 + 2][i] * inv,
-                          acc[e4 + 3][i] * inv};
-        *reinterpret_cast<f32x4*>(dst + e4) = v4;
+    for (int i = 0; i < 4; ++i) {
+      const int h = 16 * rg + 4 * grp + i;
+      const float lh = __shfl(l_run[rg], 4 * grp + i);
+      const float inv = lh > 0.f ? 1.f / lh : 0.f;
+      if (row_valid(h)) {
+        float* dst = a.o_part + (out_row(h) * ns + split) * D + c0 + kVE * col;
+#pragma unroll
+        for (int e4 = 0; e4 < kVE; e4 += 4) {
+          const f32x4 v4 = {acc[rg][e4][i] * inv, acc[rg][e4 + 1][i] * inv,
+                            acc[rg][e4 + 2][i] * inv, acc[rg][e4 + 3][i] * inv};
+          *reinterpret_cast<f32x4*>(dst + e4) = v4;
+        }
       }
     }
-  }
-  if (wave == 0 && lane < 16 && row_valid(lane)) {
-    const float lse = (m_run == -INFINITY) ? -INFINITY : (m_run + __log2f(l_run)) * kLn2;
-    a.lse_part[out_row(lane) * ns + split] = lse;
+  if (wave == 0 && lane < 16) {
+#pragma unroll
+    for (int rg = 0; rg < RG; ++rg) {
+      if (row_valid(16 * rg + lane)) {
+        const float lse = (m_run[rg] == -INFINITY) ? -INFINITY
+                                                   : (m_run[rg] + __log2f(l_run[rg])) * kLn2;
+        a.lse_part[out_row(16 * rg + lane) * ns + split] = lse;
+      }
+    }
   }
 }
 
 template <int D, int G, bool SHARED>
-const void* kernel_for(bool general) {
+const void* kernel_for(bool general, int row_groups) {
   constexpr int kSub = DECODE_ATTN_STAGE1_SUB;
-  return general ? reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, SHARED, true>)
-                 : reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, SHARED, false>);
+  if (!general) return reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, SHARED, false, 1>);
+  return row_groups == 2
+             ? reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, SHARED, true, 2>)
+             : reinterpret_cast<const void*>(&stage1_kernel<D, G, kSub, SHARED, true, 1>);
 }
 
 template <int D, int G>
@@ -470,10 +519,12 @@ hipError_t launch(const Stage1Args& args, bool shared, int batch, hipStream_t st
   // Query blocks of one split are num_splits workgroups apart, so with a split count that is a
   // multiple of 8 they land on the same XCD and share its L2 for the tiles they both read.
   dim3 grid(args.num_splits * args.num_qblocks, args.num_kv_heads, batch);
-  dim3 block(Shape<D>::kThreads);
   void* kargs[] = {const_cast<Stage1Args*>(&args)};
   const bool general = args.q_len > 1 || args.sink > 0;
-  const void* fn = shared ? kernel_for<D, G, true>(general) : kernel_for<D, G, false>(general);
+  const int rgs = stage1_row_groups(G, args.q_len);
+  dim3 block(rgs == 2 ? Shape<D, 2>::kThreads : Shape<D, 1>::kThreads);
+  const void* fn =
+      shared ? kernel_for<D, G, true>(general, rgs) : kernel_for<D, G, false>(general, rgs);
   return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
 }
 
