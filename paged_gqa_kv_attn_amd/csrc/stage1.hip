@@ -92,6 +92,45 @@ __device__ __forceinline__ void lds_barrier() {
   compiler_fence();
 }
 
+#ifndef DECODE_ATTN_PERMLANE
+#define DECODE_ATTN_PERMLANE 1
+#endif
+
+// Reductions of a value with its copies in lanes l ^ 16 and l ^ 32 (the four lanes holding one
+// head's keys). gfx950's row-swap permutes (v_permlane16/32_swap) exchange the two halves of a
+// 32-lane (or 64-lane) span in the VALU; each lane then holds the pair {x[l], x[l ^ 16]} (resp.
+// ^ 32) and combines it, with no LDS round trip as ds_bpermute would need.
+__device__ __forceinline__ float max_xor16_32(float v) {
+#if DECODE_ATTN_PERMLANE
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const float m16 = fmaxf(__builtin_bit_cast(float, (uint32_t)r16[0]),
+                          __builtin_bit_cast(float, (uint32_t)r16[1]));
+  const uint32_t c = __builtin_bit_cast(uint32_t, m16);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r32[0]),
+               __builtin_bit_cast(float, (uint32_t)r32[1]));
+#else
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+#endif
+}
+
+__device__ __forceinline__ float sum_xor16_32(float v) {
+#if DECODE_ATTN_PERMLANE
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const float s16 = __builtin_bit_cast(float, (uint32_t)r16[0]) +
+                    __builtin_bit_cast(float, (uint32_t)r16[1]);
+  const uint32_t c = __builtin_bit_cast(uint32_t, s16);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r32[0]) + __builtin_bit_cast(float, (uint32_t)r32[1]);
+#else
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+#endif
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
   return (uint32_t)__builtin_bit_cast(uint16_t, a) |
@@ -387,8 +426,7 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
           s2[u][i] = att ? sc[u][rg][i] * a.scale_log2 : -INFINITY;
           mt = fmaxf(mt, s2[u][i]);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_xor16_32(mt);
       const float m_new = fmaxf(m_run[rg], mt);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       alpha[rg] = __builtin_amdgcn_exp2f(m_run[rg] - m_use);
@@ -403,8 +441,7 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
         const u32x2 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
         pop[u][rg] = __builtin_bit_cast(i16x4, pa);
       }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
+      ps = sum_xor16_32(ps);
       l_run[rg] = l_run[rg] * alpha[rg] + ps;
       m_run[rg] = m_new;
 
