@@ -276,7 +276,13 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
 
   // Per-lane element offsets inside a tile: K (A operand) row = col, columns c0 + 32j + 8grp;
   // V rows 4grp + i, columns c0 + kVE*col .. + kVE.
-  const int k_off = col * D + c0 + 8 * grp;
+  // SHARED reads K in row order instead: load j brings rows kRPI*j + lane / kCPR, 16-byte chunk
+  // lane % kCPR, so every load covers whole 128-byte lines (the A-operand order touches half a
+  // line per row per load); the A and V operand layouts are then read back from LDS.
+  constexpr int kCPR = kCols / 8;   // 16-byte chunks in a row of this wave's columns
+  constexpr int kRPI = 64 / kCPR;   // rows per load instruction
+  const int k_off = SHARED ? (lane / kCPR) * D + c0 + 8 * (lane % kCPR) : col * D + c0 + 8 * grp;
+  const int k_step = SHARED ? kRPI * D : 32;  // element offset between the kKSteps loads
   const int v_off = (4 * grp) * D + c0 + kVE * col;
 
   // Tiles past the split re-read its last tile (an L2 hit; they are masked) so every load is
@@ -310,7 +316,7 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
   for (int u = 0; u < SUB; ++u)
 #pragma unroll
     for (int j = 0; j < kKSteps; ++j)
-      r.k[u][j] = load_stream<bf16x8>(a.k_pool + base[u] + k_off + 32 * j);
+      r.k[u][j] = load_stream<bf16x8>(a.k_pool + base[u] + k_off + k_step * j);
   if constexpr (!SHARED) {
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
@@ -336,6 +342,53 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
 
   int buf = 0;
   for (int t0 = t_begin; t0 < t_end; t0 += SUB) {
+    // Next step's K into the registers once they are consumed, then the page ids of the step
+    // after. The scheduling barriers keep loads in program order, which the wait counts rely on.
+    const int tn = t0 + SUB;
+    bool ok_n[SUB];
+    size_t base_n[SUB];
+    int32_t pid_after;
+    auto refill_k = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+        base_n[u] = tile_base(tn + u, __builtin_amdgcn_readlane(pid_next, u), ok_n[u]);
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j)
+          r.k[u][j] = load_stream<bf16x8>(a.k_pool + base_n[u] + k_off + k_step * j);
+      pid_after = load_page_ids(tn + SUB);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // A operand of the scores: K rows col, columns 32j + 8grp. SHARED parks the row-order K of
+    // this step in LDS (where P.V also reads it as V), refills the registers at once and reads
+    // the A layout back; LDS accesses of one wave take effect in program order.
+    bf16x8 ka[SUB][kKSteps];
+    if constexpr (SHARED) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j)
+          *reinterpret_cast<bf16x8*>(
+              &kv_lds[SHARED ? wave : 0][u][kRPI * j + lane / kCPR][8 * (lane % kCPR)]) =
+              r.k[u][j];
+      compiler_fence();
+      refill_k();
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j)
+          ka[u][j] = *reinterpret_cast<const bf16x8*>(
+              &kv_lds[SHARED ? wave : 0][u][col][32 * j + 8 * grp]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int j = 0; j < kKSteps; ++j) ka[u][j] = r.k[u][j];
+    }
+
     // Partial scores of this wave's columns for the SUB tiles of the step.
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
@@ -344,40 +397,15 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
         f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < kKSteps; j += 2) {
-          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[u][j], qop[rg][j], p0, 0, 0, 0);
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][j], qop[rg][j], p0, 0, 0, 0);
           if (j + 1 < kKSteps)
-            p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(r.k[u][j + 1], qop[rg][j + 1], p1, 0, 0,
+            p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[u][j + 1], qop[rg][j + 1], p1, 0, 0,
                                                          0);
         }
         score_lds[buf][u][rg][wave][lane] = p0 + p1;
       }
-      if constexpr (SHARED) {
-        // Park this wave's K slice of tile u (row col, columns 32j + 8grp) before the registers
-        // are refilled; P.V reads it back as V.
-#pragma unroll
-        for (int j = 0; j < kKSteps; ++j)
-          *reinterpret_cast<bf16x8*>(&kv_lds[SHARED ? wave : 0][u][col][32 * j + 8 * grp]) =
-              r.k[u][j];
-        compiler_fence();
-      }
     }
-
-    // Next step's K into the registers just consumed, then the page ids of the step after. The
-    // scheduling barriers keep loads in program order, which the wait counts rely on.
-    __builtin_amdgcn_sched_barrier(0);
-    const int tn = t0 + SUB;
-    bool ok_n[SUB];
-    size_t base_n[SUB];
-#pragma unroll
-    for (int u = 0; u < SUB; ++u)
-      base_n[u] = tile_base(tn + u, __builtin_amdgcn_readlane(pid_next, u), ok_n[u]);
-#pragma unroll
-    for (int u = 0; u < SUB; ++u)
-#pragma unroll
-      for (int j = 0; j < kKSteps; ++j)
-        r.k[u][j] = load_stream<bf16x8>(a.k_pool + base_n[u] + k_off + 32 * j);
-    const int32_t pid_after = load_page_ids(tn + SUB);
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!SHARED) refill_k();
 
     lds_barrier();
     f32x4 sc[SUB][RG];
