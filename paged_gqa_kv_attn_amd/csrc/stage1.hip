@@ -182,7 +182,11 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
 
   __shared__ __attribute__((aligned(16))) f32x4 score_lds[2][SUB][RG][kWaves][64];
   constexpr int kKvRow = Sh::kCols + 8;  // padded row of a parked K slice (bf16 elements)
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[SHARED ? kWaves : 1][SUB][16][kKvRow];
+  // K in row order through LDS (whole 128-byte lines per load; the A-operand order reads half a
+  // line per row per load, which doubles the L2 requests): always for SHARED, and for separate
+  // pools with one row group. With two row groups the extra LDS round trip measured slower.
+  constexpr bool KROW = SHARED || RG == 1;
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[KROW ? kWaves : 1][SUB][16][kKvRow];
 
   const int ns = a.num_splits;
   const int split = GENERAL ? (int)blockIdx.x % ns : (int)blockIdx.x;
@@ -276,13 +280,13 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
 
   // Per-lane element offsets inside a tile: K (A operand) row = col, columns c0 + 32j + 8grp;
   // V rows 4grp + i, columns c0 + kVE*col .. + kVE.
-  // SHARED reads K in row order instead: load j brings rows kRPI*j + lane / kCPR, 16-byte chunk
-  // lane % kCPR, so every load covers whole 128-byte lines (the A-operand order touches half a
-  // line per row per load); the A and V operand layouts are then read back from LDS.
+  // KROW reads K in row order instead: load j brings rows kRPI*j + lane / kCPR, 16-byte chunk
+  // lane % kCPR, so every load covers whole 128-byte lines; the A operand layout (and, for
+  // SHARED, the V layout) is then read back from LDS.
   constexpr int kCPR = kCols / 8;   // 16-byte chunks in a row of this wave's columns
   constexpr int kRPI = 64 / kCPR;   // rows per load instruction
-  const int k_off = SHARED ? (lane / kCPR) * D + c0 + 8 * (lane % kCPR) : col * D + c0 + 8 * grp;
-  const int k_step = SHARED ? kRPI * D : 32;  // element offset between the kKSteps loads
+  const int k_off = KROW ? (lane / kCPR) * D + c0 + 8 * (lane % kCPR) : col * D + c0 + 8 * grp;
+  const int k_step = KROW ? kRPI * D : 32;  // element offset between the kKSteps loads
   const int v_off = (4 * grp) * D + c0 + kVE * col;
 
   // Tiles past the split re-read its last tile (an L2 hit; they are masked) so every load is
@@ -362,17 +366,17 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // A operand of the scores: K rows col, columns 32j + 8grp. SHARED parks the row-order K of
-    // this step in LDS (where P.V also reads it as V), refills the registers at once and reads
-    // the A layout back; LDS accesses of one wave take effect in program order.
+    // A operand of the scores: K rows col, columns 32j + 8grp. KROW parks the row-order K of this
+    // step in LDS (where P.V also reads it as V when SHARED), refills the registers at once and
+    // reads the A layout back; LDS accesses of one wave take effect in program order.
     bf16x8 ka[SUB][kKSteps];
-    if constexpr (SHARED) {
+    if constexpr (KROW) {
 #pragma unroll
       for (int u = 0; u < SUB; ++u)
 #pragma unroll
         for (int j = 0; j < kKSteps; ++j)
           *reinterpret_cast<bf16x8*>(
-              &kv_lds[SHARED ? wave : 0][u][kRPI * j + lane / kCPR][8 * (lane % kCPR)]) =
+              &kv_lds[KROW ? wave : 0][u][kRPI * j + lane / kCPR][8 * (lane % kCPR)]) =
               r.k[u][j];
       compiler_fence();
       refill_k();
@@ -381,7 +385,7 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
 #pragma unroll
         for (int j = 0; j < kKSteps; ++j)
           ka[u][j] = *reinterpret_cast<const bf16x8*>(
-              &kv_lds[SHARED ? wave : 0][u][col][32 * j + 8 * grp]);
+              &kv_lds[KROW ? wave : 0][u][col][32 * j + 8 * grp]);
     } else {
 #pragma unroll
       for (int u = 0; u < SUB; ++u)
@@ -405,7 +409,7 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
         score_lds[buf][u][rg][wave][lane] = p0 + p1;
       }
     }
-    if constexpr (!SHARED) refill_k();
+    if constexpr (!KROW) refill_k();
 
     lds_barrier();
     f32x4 sc[SUB][RG];
@@ -493,7 +497,7 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           vr[i] = *reinterpret_cast<const VRow*>(
-              &kv_lds[SHARED ? wave : 0][u][4 * grp + i][kVE * col]);
+              &kv_lds[KROW ? wave : 0][u][4 * grp + i][kVE * col]);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) vr[i] = r.v[u][i];
@@ -531,9 +535,8 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           r.v[u][i] = load_stream<VRow>(a.v_pool + base_n[u] + v_off + i * D);
-    } else {
-      compiler_fence();  // this step's LDS reads stay before the next step's writes
     }
+    if constexpr (KROW) compiler_fence();  // this step's LDS reads stay before the next writes
 #pragma unroll
     for (int u = 0; u < SUB; ++u) ok[u] = ok_n[u];
     pid_next = pid_after;
