@@ -236,3 +236,36 @@ def test_status_strings(lib):
         assert binding.decode_attn_status_str(code).startswith(binding.STATUS_NAMES[code])
     assert "unknown" in binding.decode_attn_status_str(99)
     assert binding.decode_attn_version() >= 100
+
+
+def test_binding_rejects_tensors_smaller_than_the_plan():
+    """The C side takes raw pointers and cannot see tensor sizes; the binding checks element
+    counts against the plan before anything reaches the library (CPU tensors suffice: the size
+    check runs first)."""
+    import torch
+    p = plan(batch=2, max_pages_per_seq=8, num_pages=16, max_ctx_len=128, q_len=3)
+    L, Hq, Hkv, D, S = 3, 16, 2, 512, 16
+    q = torch.zeros((2, L, Hq, D), dtype=torch.bfloat16)
+    pool = torch.zeros((16, Hkv, S, D), dtype=torch.bfloat16)
+    bt = torch.zeros((2, 8), dtype=torch.int32)
+    ctx = torch.zeros((2,), dtype=torch.int32)
+    out = torch.zeros((2, L, Hq, D))
+    short = dict(q=q[:, :2].contiguous(), k_pool=pool[:15].contiguous(), block_table=bt[:, :7],
+                 ctx_lens=ctx[:1], out=out[:1])
+    for name, bad in short.items():
+        args = dict(q=q, k_pool=pool, v_pool=pool, block_table=bt, ctx_lens=ctx, out=out)
+        args[name] = bad
+        with pytest.raises(ValueError, match=name):
+            binding.decode_attn_global(p, args["q"], args["k_pool"], args["v_pool"],
+                                       args["block_table"], args["ctx_lens"], 2, 0.1,
+                                       args["out"])
+    with pytest.raises(ValueError, match="lse_out"):
+        binding.decode_attn_global(p, q, pool, pool, bt, ctx, 2, 0.1, out,
+                                   torch.zeros((2, L, Hq - 1)))
+    with pytest.raises(ValueError, match="k_new"):
+        binding.decode_attn_append_kv(p, torch.zeros((2, L - 1, Hkv, D), dtype=torch.bfloat16),
+                                      None, pool, pool, bt, ctx, 2)
+    # a smaller batch needs fewer elements: passes the size check, then fails as a host tensor
+    with pytest.raises(ValueError, match="device memory"):
+        binding.decode_attn_global(p, q[:1].contiguous(), pool, pool, bt[:1], ctx[:1], 1, 0.1,
+                                   out[:1])
