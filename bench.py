@@ -16,7 +16,6 @@ CPU oracle timed on this host's cores on the same inputs (which also checks the 
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -30,17 +29,17 @@ METRIC = "decode-attention µs/call and achieved HBM GB/s (% of peak) at 1K–12
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(ROOT, "paged_gqa_kv_attn_amd", "csrc", "*"))):
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
+def library_hash() -> str:
+    """First 16 hex digits of the SHA-256 of the built library (the build is deterministic, so
+    source edits that do not change the code keep the hash)."""
+    import paged_gqa_kv_attn_amd as pda
+    with open(pda.library_path(), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
 def load_traffic(workload: str):
-    """HBM bytes per stage-1 launch from the committed counter summary, if it was taken on the
-    current kernel sources (else None)."""
+    """HBM bytes per stage-1 launch from the committed counter summary, if it was taken with the
+    library as built now (else None)."""
     path = os.path.join(ROOT, "profiles", "stage1_global_%s_traffic.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -49,7 +48,7 @@ def load_traffic(workload: str):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_sources_sha256_16") != kernel_source_hash():
+    if fields.get("library_sha256_16") != library_hash():
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -315,7 +314,7 @@ def main() -> int:
         }
         result["parity_vs_oracle"] = {"max_abs_err": err, "min_cos": cos}
 
-    result["kernel_sources_sha256_16"] = kernel_source_hash()
+    result["library_sha256_16"] = library_hash()
     print(json.dumps(result), flush=True)
     return 0
 

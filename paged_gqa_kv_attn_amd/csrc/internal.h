@@ -10,19 +10,18 @@ namespace decode_attn {
 constexpr uint32_t kPlanMagic = 0x44415431u;  // "DAT1"
 constexpr int kTile = 16;                     // keys per tile: the M dimension of one MFMA
 constexpr int kDefaultMaxSplits = 256;
-constexpr int kMinTilesPerSplit = 2;          // 32 keys: one stage-1 loop step
-constexpr int kStage1Threads = 256;           // 4 wavefronts of 64 lanes
+constexpr int kMinTilesPerSplit = 2;          // 32 keys per chunk at least
 constexpr int kStage2Threads = 256;
 
-// Kernel arguments of stage 1 (one workgroup per (split, kv head, sequence)).
+// Kernel arguments of stage 1 (one workgroup per (split, query block, kv head, sequence)).
 struct Stage1Args {
-  const uint16_t* q;            // [B, Hq, D] bf16
+  const uint16_t* q;            // [B, L, Hq, D] bf16
   const uint16_t* k_pool;       // [P, Hkv, S, D] bf16
   const uint16_t* v_pool;       // [P, Hkv, S, D] bf16
   const int32_t* block_table;   // [B, max_pages_per_seq]
   const int32_t* ctx_lens;      // [B]
-  float* o_part;                // [B, Hq, num_splits, D]
-  float* lse_part;              // [B, Hq, num_splits]
+  float* o_part;                // [B, L, Hq, num_splits, D]
+  float* lse_part;              // [B, L, Hq, num_splits]
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t page_size;
@@ -37,17 +36,18 @@ struct Stage1Args {
 };
 
 // Kernel arguments of stage 2 (one workgroup per (64-wide slice of D, q head, sequence)).
+// B' = B * L rows of Hq query heads (the query tokens of a sequence are consecutive rows).
 struct Stage2Args {
-  const float* o_part;          // [B, Hq, num_splits, D]
-  const float* lse_part;        // [B, Hq, num_splits]
-  float* out;                   // [B, Hq, D]
-  float* lse_out;               // [B, Hq] or nullptr
+  const float* o_part;          // [B', Hq, num_splits, D]
+  const float* lse_part;        // [B', Hq, num_splits]
+  float* out;                   // [B', Hq, D]
+  float* lse_out;               // [B', Hq] or nullptr
   int32_t num_q_heads;
   int32_t head_dim;
   int32_t num_splits;
 };
 
-// Kernel arguments of the paged KV append (one workgroup per (sequence, KV head)).
+// Kernel arguments of the paged KV append (one workgroup per (sequence, new token, KV head)).
 struct AppendArgs {
   const uint16_t* k_new;        // [B, L, Hkv, D] bf16
   const uint16_t* v_new;        // [B, L, Hkv, D] bf16 (unused when v_pool == k_pool)

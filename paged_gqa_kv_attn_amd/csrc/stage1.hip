@@ -1,10 +1,10 @@
 // stage1.hip — split-KV stage 1 of paged GQA decode attention for gfx950 (CDNA4).
 //
-// One workgroup per (split, kv head, sequence) reads the keys of its chunk once and serves every
-// query head of the GQA group with them (several query heads sharing a KV head are handled by
-// one program: Sparse-vLLM PR #27 "feat: support Gemma 4 and native multimodal inference",
-// section "专用算子与性能优化"). It writes the chunk's softmax-normalised partial output and its
-// log-sum-exp, the split-KV partial buffer of vLLM learning notes "模型库与算子层 — 概念",
+// One workgroup per (split, query block, kv head, sequence) reads the keys of its chunk once and
+// serves every query head of the GQA group with them (several query heads sharing a KV head are
+// handled by one program: Sparse-vLLM PR #27 "feat: support Gemma 4 and native multimodal
+// inference", section "专用算子与性能优化"). It writes the chunk's softmax-normalised partial output
+// and its log-sum-exp, the split-KV partial buffer of vLLM learning notes "模型库与算子层 — 概念",
 // section "MLA 与 Sparse MLA（DSA）".
 //
 // Work decomposition (NW = D / CW wavefronts of 64 lanes, each owning CW head-dim columns: CW = 128
@@ -12,22 +12,25 @@
 // a tile being a page of 16 keys or a 16-key slice of a larger page; all waves work on the same
 // tiles):
 //   * wave w owns the head-dim columns [CW*w, CW*w + CW) of K, V and the output;
-//   * scores: v_mfma_f32_16x16x32_bf16 with A = K tile (16 keys x 32 columns; every lane loads 16
-//     contiguous bytes of one key row straight from HBM) and B = the q group (32 columns x 16
-//     heads, heads >= G zero, kept in registers). Each wave gets the partial scores of its
-//     columns; the NW partials meet in LDS (one barrier per step) and are summed in a fixed
-//     order, so every wave holds the same full scores: lane l has keys 4*(l/16)..+3 of head l%16;
-//   * softmax: keys outside [lo, n) get -inf by select (never by multiplying a mask, so NaN in
-//     unused slots cannot leak), running max and sum per head in base-2 units, hardware exp2;
-//   * P.V: v_mfma_f32_16x16x16_bf16 with A = P (16 heads x 16 keys, which is exactly the layout the
+//   * scores: v_mfma_f32_16x16x32_bf16 with A = K tile (16 keys x 32 columns) and B = the q block
+//     (32 columns x 16 rows, one row per (query, head), unused rows zero, kept in registers). K is
+//     loaded in row order, whole 128-byte lines per load, parked in the wave's LDS slice and read
+//     back in the A layout (two-row-group blocks load the A layout directly). Each wave gets the
+//     partial scores of its columns; the NW partials meet in LDS (one barrier per step) and are
+//     summed in a fixed order, so every wave holds the same full scores: lane l has keys
+//     4*(l/16)..+3 of row l%16;
+//   * softmax: keys a row does not attend get -inf by select (never by multiplying a mask, so NaN
+//     in unused slots cannot leak), running max and sum per row in base-2 units, hardware exp2,
+//     the four lanes of a row combined with row-half swaps (v_permlane16/32_swap);
+//   * P.V: v_mfma_f32_16x16x16_bf16 with A = P (16 rows x 16 keys, which is exactly the layout the
 //     score MFMA left in the lanes, rounded to bf16) and B = V (16 keys x 16 columns). V is loaded
 //     so that lane l holds CW/8 bytes of keys 4*(l/16)..+3 in its own column slice and is
-//     transposed inside the lane with byte permutes; each wave accumulates O[heads][its columns];
+//     transposed inside the lane with byte permutes; each wave accumulates O[rows][its columns];
 //   * loads run one step ahead in registers: the K registers are refilled for the next step right
-//     after the score MFMAs, the V registers right after the P.V MFMAs; the page ids of the step
-//     after that are fetched as a small vector (lane u holds tile u's id) one step earlier still,
-//     so no dependent block-table read sits on the critical path.
-// The per-head softmax state is identical in all waves, so no merge is needed at the end: each
+//     after the park (or the score MFMAs), the V registers right after the P.V MFMAs; the page ids
+//     of the step after that are fetched as a small vector (lane u holds tile u's id) one step
+//     earlier still, so no dependent block-table read sits on the critical path.
+// The per-row softmax state is identical in all waves, so no merge is needed at the end: each
 // wave writes its own columns of the partial output.
 
 #include <hip/hip_runtime.h>
@@ -97,7 +100,7 @@ __device__ __forceinline__ void lds_barrier() {
 #endif
 
 // Reductions of a value with its copies in lanes l ^ 16 and l ^ 32 (the four lanes holding one
-// head's keys). gfx950's row-swap permutes (v_permlane16/32_swap) exchange the two halves of a
+// row's keys). gfx950's row-swap permutes (v_permlane16/32_swap) exchange the two halves of a
 // 32-lane (or 64-lane) span in the VALU; each lane then holds the pair {x[l], x[l ^ 16]} (resp.
 // ^ 32) and combines it, with no LDS round trip as ds_bpermute would need.
 __device__ __forceinline__ float max_xor16_32(float v) {
@@ -167,7 +170,7 @@ struct StepRegs {
 
 // SHARED: the pools are one buffer (layers whose values are their keys). Each tile is then read
 // once; every wave parks its K slice in LDS (rows padded by 16 bytes against bank conflicts) and
-// reads it back in the V operand layout.
+// reads it back in both operand layouts.
 // GENERAL: several query tokens per sequence and/or sink keys. Without it (one query token, no
 // sinks) the row bounds are uniform and the query-block and sink arithmetic folds away.
 // RG: groups of 16 MFMA rows per workgroup (2 only with GENERAL): 16 * RG rows share every tile
