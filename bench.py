@@ -29,17 +29,26 @@ METRIC = "decode-attention µs/call and achieved HBM GB/s (% of peak) at 1K–12
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 
 
-def library_hash() -> str:
-    """First 16 hex digits of the SHA-256 of the built library (the build is deterministic, so
-    source edits that do not change the code keep the hash)."""
+def kernel_code_hash() -> str:
+    """First 16 hex digits of the SHA-256 of the library's device code (its .hip_fatbin ELF
+    section): host-side edits and comment edits leave it unchanged, kernel edits do not."""
+    import struct
     import paged_gqa_kv_attn_amd as pda
     with open(pda.library_path(), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+        elf = f.read()
+    shoff, = struct.unpack_from("<Q", elf, 0x28)
+    shentsize, shnum, shstrndx = struct.unpack_from("<HHH", elf, 0x3A)
+    sections = [struct.unpack_from("<IIQQQQ", elf, shoff + i * shentsize) for i in range(shnum)]
+    names = sections[shstrndx][4]
+    for name, _, _, _, offset, size in sections:
+        if elf[names + name:elf.index(b"\0", names + name)] == b".hip_fatbin":
+            return hashlib.sha256(elf[offset:offset + size]).hexdigest()[:16]
+    raise RuntimeError("no device code section in %s" % pda.library_path())
 
 
-def load_traffic(workload: str):
+def load_traffic(workload: str, num_splits: int):
     """HBM bytes per stage-1 launch from the committed counter summary, if it was taken with the
-    library as built now (else None)."""
+    same device code and split count as now (else None)."""
     path = os.path.join(ROOT, "profiles", "stage1_global_%s_traffic.txt" % workload)
     if not os.path.exists(path):
         return None
@@ -48,7 +57,9 @@ def load_traffic(workload: str):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("library_sha256_16") != library_hash():
+    if fields.get("kernel_code_sha256_16") != kernel_code_hash():
+        return None
+    if fields.get("num_splits") != str(num_splits):
         return None
     try:
         return int(fields["hbm_bytes_per_launch"])
@@ -224,7 +235,7 @@ def main() -> int:
     s1_bytes = dominant["bytes"] - gd["B"] * args.q_len * gd["Hq"] * gd["D"] * 4  # minus out
     achieved = s1_bytes / (s1_avg_us * 1e-6) / 1e9
     plain = args.q_len == 1 and args.sink == 0 and not args.k_eq_v
-    traffic = load_traffic(args.workload) if plain else None
+    traffic = load_traffic(args.workload, dominant["plan"].num_splits) if plain else None
 
     result = {
         "metric": METRIC,
@@ -314,7 +325,7 @@ def main() -> int:
         }
         result["parity_vs_oracle"] = {"max_abs_err": err, "min_cos": cos}
 
-    result["library_sha256_16"] = library_hash()
+    result["kernel_code_sha256_16"] = kernel_code_hash()
     print(json.dumps(result), flush=True)
     return 0
 

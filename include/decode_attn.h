@@ -136,9 +136,10 @@ typedef struct {
  * + ceil(sink / 16) for its sink keys) tiles of 16 keys for the longest range one query block
  * walks, e = min(max_ctx_len, W + min(L, Q) - 1 or unlimited), with Q the queries of a block,
  * pairs = batch * Hkv * ceil(L / Q) and target = num_cus workgroups for head_dim 512 with
- * separate pools (2 * num_cus for head_dim 256 or when values are keys),
+ * separate pools and G * L <= 16 (2 * num_cus for head_dim 256, when values are keys, or for
+ * blocks of 32 rows),
  *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, ceil(T / 2)))
- * so every chunk holds at least 2 tiles (32 keys, one stage-1 loop step) when the context
+ * so every chunk holds at least 2 tiles (32 keys) when the context
  * allows it.
  * Returns DECODE_ATTN_OK, DECODE_ATTN_ERR_NULL, _SHAPE, _UNSUPPORTED or _HIP (device query).
  */

@@ -218,8 +218,11 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   // smaller heads (short per-workgroup chunks, more latency to hide).
   // A layer whose values are its keys reads half the bytes per tile and needs twice the
   // workgroups in flight to stay fed (measured: 1 per CU 88 us, 2 per CU 66 us, 4 per CU 80 us).
+  // Blocks with two row groups (G * q_len > 16) do twice the MFMA and softmax work per tile and
+  // likewise run best at two per CU (measured: 4 tokens on the 32K global layer 131 -> 113 us).
+  const bool two_row_groups = stage1_row_groups(G, p.q_len) == 2;
   const int64_t target =
-      ((p.head_dim >= 512 && !p.values_are_keys) ? 1 : 2) * (int64_t)p.num_cus;
+      ((p.head_dim >= 512 && !p.values_are_keys && !two_row_groups) ? 1 : 2) * (int64_t)p.num_cus;
   int64_t splits = (target + pairs - 1) / pairs;
   int64_t cap = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
   if (cap > p.max_splits) cap = p.max_splits;
