@@ -138,9 +138,9 @@ typedef struct {
  * pairs = batch * Hkv * ceil(L / Q) and target = num_cus workgroups for head_dim 512 with
  * separate pools and G * L <= 16 (2 * num_cus for head_dim 256, when values are keys, or for
  * blocks of 32 rows),
- *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, ceil(T / 2)))
- * so every chunk holds at least 2 tiles (32 keys) when the context
- * allows it.
+ *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, T))
+ * so every chunk holds at least one tile when the context allows it (short contexts are
+ * latency-bound: more, shorter chunks finish sooner).
  * Returns DECODE_ATTN_OK, DECODE_ATTN_ERR_NULL, _SHAPE, _UNSUPPORTED or _HIP (device query).
  */
 int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* plan);

@@ -10,7 +10,7 @@ namespace decode_attn {
 constexpr uint32_t kPlanMagic = 0x44415431u;  // "DAT1"
 constexpr int kTile = 16;                     // keys per tile: the M dimension of one MFMA
 constexpr int kDefaultMaxSplits = 256;
-constexpr int kMinTilesPerSplit = 2;          // 32 keys per chunk at least
+constexpr int kMinTilesPerSplit = 1;          // a chunk holds one 16-key tile at least
 constexpr int kStage2Threads = 256;
 
 // Kernel arguments of stage 1 (one workgroup per (split, query block, kv head, sequence)).

@@ -71,15 +71,15 @@ def expected_workspace(B, Hq, ns, D, L=1):
     (dict(batch=8, max_pages_per_seq=80, max_ctx_len=1280), 16),      # 16 pairs
     (dict(num_kv_heads=8, head_dim=256, window=1024), 16),            # 65 tiles, 32 pairs
     (dict(num_kv_heads=8, head_dim=256, window=1024, sink=4), 16),    # + 1 sink tile
-    (dict(batch=1, num_kv_heads=8, head_dim=256, window=64, max_ctx_len=8192), 3),  # 5 tiles
-    (dict(batch=1, num_kv_heads=8, head_dim=256, window=64, max_ctx_len=8192, sink=40), 4),
+    (dict(batch=1, num_kv_heads=8, head_dim=256, window=64, max_ctx_len=8192), 5),  # 5 tiles
+    (dict(batch=1, num_kv_heads=8, head_dim=256, window=64, max_ctx_len=8192, sink=40), 8),
     (dict(q_len=4), 64),                                              # 32 rows: 1 block, 2/CU
     (dict(q_len=8), 32),                                              # 2 blocks of 4 queries
     (dict(q_len=2), 32),                                              # 1 block: as q_len 1
     (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024,
-          q_len=8), 32),                                              # G 4: capped by tiles
-    (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024), 32),
-    (dict(batch=1, max_pages_per_seq=4, max_ctx_len=64), 2),          # capped: >= 2 tiles/split
+          q_len=8), 64),                                              # G 4: capped by tiles
+    (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024), 64),
+    (dict(batch=1, max_pages_per_seq=4, max_ctx_len=64), 4),          # capped: >= 1 tile/split
 ])
 def test_plan_split_counts(kw, splits):
     p = plan(**kw)
