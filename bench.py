@@ -220,6 +220,8 @@ def main() -> int:
         us = sorted(1e3 * ea.elapsed_time(eb) for ea, eb in evs)
         med = us[len(us) // 2]
         detail[L["kind"]] = {"us_per_call_median": round(med, 2),
+                             "us_per_call_p10": round(us[len(us) // 10], 2),
+                             "us_per_call_p90": round(us[(9 * len(us)) // 10], 2),
                              "GB_per_s": round(L["bytes"] / (med * 1e-6) / 1e9, 1),
                              "pct_of_hbm_peak": round(100 * L["bytes"] / (med * 1e-6) / 1e9 /
                                                       PEAK_HBM_GBS, 2)}
@@ -324,6 +326,17 @@ def main() -> int:
             "cpu_model": _cpu_model(),
         }
         result["parity_vs_oracle"] = {"max_abs_err": err, "min_cos": cos}
+        # The same oracle on one host thread, one step (context for the all-cores figure).
+        t_a = time.perf_counter()
+        for h in host:
+            oracle.decode_attn_multi(h.q if h.q_len > 1 else h.q[:, None], h.k_pool, h.v_pool,
+                                     h.block_table, h.ctx_lens, h.scale, h.window, h.sink,
+                                     num_threads=1)
+        one = time.perf_counter() - t_a
+        result["cpu_baseline_one_thread"] = {
+            "value": round(step_bytes / one / 1e9, 3), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "sample": "1 full %s step (all layers), fp64 oracle, %.1f s" % (
+                args.workload, one)}
 
     result["kernel_code_sha256_16"] = kernel_code_hash()
     print(json.dumps(result), flush=True)

@@ -199,7 +199,7 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int grp = lane >> 4;  // lane group 0..3
-  const int col = lane & 15;  // column (scores: head; P.V: column block)
+  const int col = lane & 15;  // scores: MFMA row (query, head); P.V: column block
   const int S = a.page_size;
   constexpr int kCols = Sh::kCols;
   using VRow = typename Sh::VRow;
