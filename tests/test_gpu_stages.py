@@ -51,6 +51,83 @@ def test_stage1_partials_match_oracle_chunks(D, G, window):
         gu.compare(o_part[:, :, s], lse_part[:, :, s], ref[0], ref[1], "split %d" % s)
 
 
+def split_keysets(n_ctx, L, G, window, sink, ns):
+    """Keys each (query, split) attends in stage 1, as the header documents it: queries in blocks
+    of 16 / G (32 / G when G * L > 16); a block walks the sink tiles, then its window's tiles, and
+    split s takes list entries [floor(s T / ns), floor((s + 1) T / ns)); a query keeps the keys of
+    those tiles that it attends."""
+    per = (32 if G * L > 16 and L > 1 else 16) // G
+    sink = sink if window > 0 else 0
+    end = lambda i: max(0, n_ctx - L + i + 1)
+    wlo = lambda e: e - window if window > 0 and e > window else 0
+    sets = {}
+    for first in range(0, L, per):
+        last = min(L, first + per) - 1
+        n, lo = end(last), wlo(end(first))
+        sk = min(sink, lo)
+        st = -(-sk // 16)
+        w0 = max(st, lo // 16)
+        T = st + max(0, -(-n // 16) - w0)
+        for sp in range(ns):
+            tiles = [e if e < st else e - st + w0 for e in range(sp * T // ns, (sp + 1) * T // ns)]
+            keys = {t for p in tiles for t in range(16 * p, 16 * p + 16)}
+            for i in range(first, last + 1):
+                ni, li = end(i), wlo(end(i))
+                sets[i, sp] = sorted(t for t in keys if t < ni and (t >= li or t < sink))
+    return sets
+
+
+def runs(keys):
+    out = []
+    for t in keys:
+        if out and out[-1][1] == t:
+            out[-1][1] = t + 1
+        else:
+            out.append([t, t + 1])
+    return out
+
+
+@pytest.mark.parametrize("D,G,L,window,sink", [(256, 2, 3, 40, 20), (512, 8, 3, 0, 0),
+                                               (256, 2, 1, 33, 17), (512, 8, 4, 100, 5)])
+def test_stage1_partials_follow_the_documented_tile_list(D, G, L, window, sink):
+    """Stage-1 partials with sinks and several query tokens: each (query, split) equals the
+    oracle over the keys the documented tile list gives it (sink and window parts merged by the
+    oracle's LSE merge)."""
+    import torch
+    gu.ensure_library()
+    ctx = [1, 30, 70, 130, 300]
+    inp = make_layer_inputs(ctx, 2 * G, 2, D, page_size=16, window=window, sink=sink,
+                            seed=[27, D, G, L], q_len=L)
+    plan = gu.make_plan(inp, force_splits=5)
+    t = gu.upload(inp)
+    ws = torch.full((plan.workspace_bytes // 4,), float("nan"), device=gu.device())
+    pda.decode_attn_stage1(plan, t["q"], t["k"], t["v"], t["bt"], t["ctx"], len(ctx), inp.scale,
+                           ws)
+    torch.cuda.synchronize()
+    ns, Hq, B = plan.num_splits, 2 * G, len(ctx)
+    rows = B * L * Hq
+    o_part = ws[: rows * ns * D].view(B, L, Hq, ns, D).cpu().numpy()
+    off = plan.partial_lse_offset // 4
+    lse_part = ws[off: off + rows * ns].view(B, L, Hq, ns).cpu().numpy()
+    q4 = inp.q if L > 1 else inp.q[:, None]
+    sets = [split_keysets(n, L, G, window, sink, ns) for n in ctx]
+    for i in range(L):
+        for sp in range(ns):
+            parts = []
+            for r in range(2):  # at most a sink run and a window run
+                lo_hi = [runs(sets[b][i, sp])[r] if len(runs(sets[b][i, sp])) > r else [0, 0]
+                         for b in range(B)]
+                parts.append(oracle.decode_attn_ranges(
+                    np.ascontiguousarray(q4[:, i]), inp.k_pool, inp.v_pool, inp.block_table,
+                    [x[0] for x in lo_hi], [x[1] for x in lo_hi], inp.scale))
+            assert all(len(runs(sets[b][i, sp])) <= 2 for b in range(B))
+            o = np.stack([p[0] for p in parts], axis=2).reshape(B * Hq, 2, D)
+            l = np.stack([p[1] for p in parts], axis=2).reshape(B * Hq, 2)
+            ref_o, ref_l = oracle.lse_merge(o, l)
+            gu.compare(o_part[:, i, :, sp], lse_part[:, i, :, sp], ref_o.reshape(B, Hq, D),
+                       ref_l.reshape(B, Hq), "query %d split %d" % (i, sp))
+
+
 @pytest.mark.parametrize("ns", [1, 3, 64, 257])
 def test_stage2_merge_matches_oracle(ns):
     import torch
