@@ -563,11 +563,17 @@ def test_golden_regression_cases():
         cases = json.load(f)["cases"]
     assert cases
     for case in cases:
+        sink, q_len = case.get("sink", 0), case.get("q_len", 1)
         inp = make_layer_inputs(case["ctx_lens"], case["Hq"], case["Hkv"], case["D"],
                                 page_size=case["S"], window=case["window"], seed=case["seed"],
-                                q_mult=case["q_mult"])
-        out, lse = oracle.decode_attn(inp.q, inp.k_pool, inp.v_pool, inp.block_table, inp.ctx_lens,
-                                      inp.scale, window=case["window"])
+                                q_mult=case["q_mult"], sink=sink, q_len=q_len)
+        if sink or q_len > 1:
+            out, lse = oracle.decode_attn_multi(inp.q if q_len > 1 else inp.q[:, None],
+                                                inp.k_pool, inp.v_pool, inp.block_table,
+                                                inp.ctx_lens, inp.scale, case["window"], sink)
+        else:
+            out, lse = oracle.decode_attn(inp.q, inp.k_pool, inp.v_pool, inp.block_table,
+                                          inp.ctx_lens, inp.scale, window=case["window"])
         np.testing.assert_allclose(out, np.array(case["out"]), rtol=0, atol=1e-12)
         np.testing.assert_allclose(lse, np.array(case["lse"]), rtol=0, atol=1e-12)
 
