@@ -219,7 +219,9 @@ int decode_attn_append_kv(const decode_attn_plan_t* plan, const void* k_new, con
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_str(int status);
 
-/* Library version, major * 10000 + minor * 100 + patch. */
+/* Library version, major * 10000 + minor * 100 + patch. The minor number changes with the layout
+ * of decode_attn_problem / decode_attn_plan_t (0.2: sink and q_len fields). */
+#define DECODE_ATTN_VERSION 200
 int decode_attn_version(void);
 
 #ifdef __cplusplus

@@ -73,6 +73,10 @@ def library_path() -> str:
     return os.environ.get("PAGED_GQA_KV_ATTN_LIB") or os.path.join(_HERE, _LIB_NAME)
 
 
+# decode_attn_version() of the library whose struct layouts Problem and Plan mirror.
+ABI_VERSION = 200
+
+
 def load_library():
     """Load ``libdecode_attn.so`` from the package directory (raises if it is not built)."""
     global _lib
@@ -104,6 +108,9 @@ def load_library():
     lib.decode_attn_status_str.restype = ctypes.c_char_p
     lib.decode_attn_version.argtypes = []
     lib.decode_attn_version.restype = ctypes.c_int
+    if lib.decode_attn_version() != ABI_VERSION:
+        raise RuntimeError("%s reports version %d; this binding's structs match version %d "
+                           "(rebuild the library)" % (path, lib.decode_attn_version(), ABI_VERSION))
     _lib = lib
     return lib
 

@@ -332,6 +332,6 @@ const char* decode_attn_status_str(int status) {
   }
 }
 
-int decode_attn_version(void) { return 100; }
+int decode_attn_version(void) { return DECODE_ATTN_VERSION; }
 
 }  // extern "C"

@@ -235,7 +235,7 @@ def test_status_strings(lib):
     for code in range(8):
         assert binding.decode_attn_status_str(code).startswith(binding.STATUS_NAMES[code])
     assert "unknown" in binding.decode_attn_status_str(99)
-    assert binding.decode_attn_version() >= 100
+    assert binding.decode_attn_version() == binding.ABI_VERSION == 200
 
 
 def test_binding_rejects_tensors_smaller_than_the_plan():
