@@ -43,6 +43,18 @@ def test_multi_every_alignment(L, window, sink):
                                                                           splits))
 
 
+@pytest.mark.parametrize("S", [32, 64, 256])
+def test_multi_larger_pages(S):
+    """Several query tokens and a sliding window with sinks over pages of 32-256 keys (tiles are
+    16-key slices of a page)."""
+    print("multi pages S=%d" % S, flush=True)
+    ctx = [3, 100, 517, 1300]
+    inp = make_layer_inputs(ctx, 16, 2, 512, page_size=S, window=300, sink=8, seed=[67, S],
+                            q_len=3)
+    out, lse = gu.run(inp, force_splits=4)
+    gu.compare(out, lse, *gu.reference(inp), "multi S%d" % S)
+
+
 def test_multi_one_query_is_bitwise_single_token():
     """A plan with q_len 1 and q given as [B, 1, Hq, D] is the single-token path, bit for bit."""
     inp = make_layer_inputs([1000, 77, 2049], 16, 2, 512, page_size=16, seed=63)
