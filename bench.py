@@ -84,6 +84,8 @@ def main() -> int:
                     help="query tokens per sequence (causal multi-token decode), both layers")
     ap.add_argument("--settle-ms", type=float, default=500.0,
                     help="untimed steps for this long before the warmup steps (clock ramp-up)")
+    ap.add_argument("--append", action="store_true",
+                    help="each layer call first appends the step's new tokens' K/V to the pools")
     ap.add_argument("--sink", type=int, default=0,
                     help="sink keys the sliding layer also attends (StreamingLLM-style view)")
     args = ap.parse_args()
@@ -143,7 +145,16 @@ def main() -> int:
                                     max_ctx_len=int(inp.ctx_lens.max()), window=inp.window,
                                     values_are_keys=args.k_eq_v, sink=sink, q_len=args.q_len)
         spec = wl.layers[kind]
+        # The newest q_len tokens' K/V as the append's input: the values already in the pools, so the
+        # appended cache (and the oracle check) is unchanged while the copy does its full work.
+        S, Lq = d["S"], args.q_len
+        pos = inp.ctx_lens[:, None] - Lq + np.arange(Lq)[None, :]
+        pages = inp.block_table[np.arange(d["B"])[:, None], pos // S]
+        k_new = np.ascontiguousarray(inp.k_pool[pages, :, pos % S, :])  # [B, L, Hkv, D]
+        v_new = np.ascontiguousarray(inp.v_pool[pages, :, pos % S, :])
         layers.append(dict(
+            k_new=bf(k_new), v_new=bf(v_new),
+            append_bytes=2 * k_new.size * 2 * (1 if args.k_eq_v else 2),
             kind=kind, inp=inp, dims=d, plan=plan, q=bf(inp.q), k=ks, v=vs,
             bt=torch.from_numpy(inp.block_table).to(dev),
             ctx=torch.from_numpy(inp.ctx_lens).to(dev),
@@ -163,8 +174,14 @@ def main() -> int:
     dominant = layers[0]  # the global layer's stage 1 moves ~all of the bytes
     B = dominant["plan"].problem.batch
 
+    def append(L, r):
+        pda.decode_attn_append_kv(L["plan"], L["k_new"], L["v_new"], L["k"][r], L["v"][r],
+                                  L["bt"], L["ctx"], L["plan"].problem.batch)
+
     def run_layer(L, r, ev_s1=None):
         p = L["plan"]
+        if args.append:
+            append(L, r)
         if L is dominant:
             if ev_s1 is not None:
                 ev_s1[0].record(stream)
@@ -219,13 +236,26 @@ def main() -> int:
         torch.cuda.synchronize()
         us = sorted(1e3 * ea.elapsed_time(eb) for ea, eb in evs)
         med = us[len(us) // 2]
+        if args.append:
+            eva = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(20)]
+            for i, (ea, eb) in enumerate(eva):
+                ea.record(stream)
+                append(L, i % R)
+                eb.record(stream)
+            torch.cuda.synchronize()
+            ua = sorted(1e3 * ea.elapsed_time(eb) for ea, eb in eva)
+            L["append_us"] = ua[len(ua) // 2]
         detail[L["kind"]] = {"us_per_call_median": round(med, 2),
                              "us_per_call_p10": round(us[len(us) // 10], 2),
                              "us_per_call_p90": round(us[(9 * len(us)) // 10], 2),
                              "GB_per_s": round(L["bytes"] / (med * 1e-6) / 1e9, 1),
                              "pct_of_hbm_peak": round(100 * L["bytes"] / (med * 1e-6) / 1e9 /
                                                       PEAK_HBM_GBS, 2)}
-    step_bytes = sum(L["bytes"] for L in layers)
+        if args.append:
+            detail[L["kind"]].update(append_us_median=round(L["append_us"], 2),
+                                     append_bytes=L["append_bytes"])
+    step_bytes = sum(L["bytes"] + (L["append_bytes"] if args.append else 0) for L in layers)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     s1_ms = [a.elapsed_time(b) for a, b in ev]
     s1_avg_us = 1e3 * sum(s1_ms) / len(s1_ms)
@@ -270,6 +300,7 @@ def main() -> int:
             "k_eq_v": bool(args.k_eq_v),
             "q_len": args.q_len,
             "sliding_sink": args.sink,
+            "append_in_step": bool(args.append),
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
