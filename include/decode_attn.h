@@ -1,8 +1,8 @@
 /*
  * decode_attn.h — C ABI of the paged GQA split-KV decode-attention library for MI355X (gfx950).
  *
- * What it computes. Single-token decode attention over a paged KV cache for the two layer kinds of
- * a Gemma-4-style model: "global" layers (every cached key attended; head_dim 512 in Gemma 4) and
+ * What it computes. Decode attention (one new query token per sequence, or up to 16 causal ones)
+ * over a paged KV cache for the two layer kinds of a Gemma-4-style model: "global" layers (every cached key attended; head_dim 512 in Gemma 4) and
  * "sliding-window" layers (only the last W keys attended; head_dim 256 in Gemma 4). The layer kinds
  * may differ in head dim, KV-head count and window (Sparse-vLLM PR #27 "feat: support Gemma 4 and
  * native multimodal inference", section "Gemma 4 文本推理" / Gemma 4 text inference). Several query
@@ -27,9 +27,9 @@
  * single-token decode that section "核心操作" of the same notes describes.
  *
  * How. Split-KV: stage 1 cuts each sequence's key range into num_splits chunks and writes, per
- * (b, h, split), the chunk's normalised partial output and its log-sum-exp; stage 2 merges the
- * partials of each (b, h) by their log-sum-exps. The partial buffer reserves one LSE value per
- * (b, h, split) next to the D partial outputs and is sized once, for the worst case, so that no
+ * (b, i, h, split), the chunk's normalised partial output and its log-sum-exp; stage 2 merges the
+ * partials of each (b, i, h) by their log-sum-exps. The partial buffer reserves one LSE value per
+ * (b, i, h, split) next to the D partial outputs and is sized once, for the worst case, so that no
  * call allocates and calls can be captured in a HIP graph (vLLM learning notes, section
  * "MLA 与 Sparse MLA（DSA）", split-KV MLA decode). A plan is computed on the host from the shape
  * only; it holds no device pointer, in particular no page-table address, so reusing a plan across
