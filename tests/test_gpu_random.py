@@ -1,7 +1,7 @@
 """GPU parity on a fixed list of seeded random configurations: every option of the path combined at
 random (head_dim, group size, page size, window, sink keys, query tokens, split count, one pool for
-K and V, ragged contexts including ones shorter than the query count), each against the fp64
-oracle. The list is generated from a fixed seed, so every run checks the same cases."""
+K and V, ragged contexts including ones shorter than the query count, query scales up to scores in
+the hundreds), each against the fp64 oracle. The list is generated from a fixed seed, so every run checks the same cases."""
 from __future__ import annotations
 
 import numpy as np
@@ -28,16 +28,17 @@ def _cases(count=120, seed=2024):
         ctx = [int(x) for x in rng.integers(1, 900, size=B)]
         splits = int(rng.choice([0, 1, 3, 7]))
         kv = bool(rng.random() < 0.25)
-        out.append((k, D, G, Hkv, S, window, sink, q_len, ctx, splits, kv))
+        q_mult = float(rng.choice([1.0, 1.0, 4.0, 30.0]))  # 30: scores in the hundreds
+        out.append((k, D, G, Hkv, S, window, sink, q_len, ctx, splits, kv, q_mult))
     return out
 
 
 @pytest.mark.parametrize("case", _cases(), ids=lambda c: "case%d" % c[0])
 def test_random_configuration(case):
-    k, D, G, Hkv, S, window, sink, q_len, ctx, splits, kv = case
+    k, D, G, Hkv, S, window, sink, q_len, ctx, splits, kv, q_mult = case
     print("random case", case, flush=True)
     inp = make_layer_inputs(ctx, G * Hkv, Hkv, D, page_size=S, window=window, sink=sink,
-                            q_len=q_len, seed=[70, k])
+                            q_len=q_len, seed=[70, k], q_mult=q_mult)
     t = None
     if kv:
         inp.v_pool = inp.k_pool
