@@ -7,8 +7,10 @@ in HBM. Default workload: long_ctx (batch 4, 33792 keys per sequence; global lay
 heads, head_dim 512; sliding layer 16 q / 8 KV heads, head_dim 256, window 1024).
 
 Prints one JSON line: whole-step algorithmic HBM GB/s (value), ms per step, the roofline of the
-dominant kernel (global stage 1: HIP events on its stream around every timed launch), and the fp64
-CPU oracle timed on this host's cores on the same inputs (which also checks the step's outputs).
+dominant kernel (global stage 1: HIP events on its stream around every timed launch), per-layer
+event medians (cold: the caches flushed before each call; hot: back to back), and the fp64 CPU
+oracle timed on this host's cores on the same inputs (which also checks the step's outputs).
+Steps rotate over copies of the KV pools so that no step finds its K/V in the L2s or the MALL.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
@@ -73,8 +75,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long_ctx")
-    ap.add_argument("--copies", type=int, default=2,
-                    help="distinct copies of the KV pools, used in rotation across steps")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="distinct copies of the KV pools, used in rotation across steps; 0 = "
+                         "enough that a step re-reads a copy only after ~768 MB of other K/V "
+                         "(more than the L2s and the 256 MB MALL hold)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -122,6 +126,13 @@ def main() -> int:
     pda.load_library()
 
     wl = wl_mod.WORKLOADS[args.workload]
+    copies = args.copies
+    if copies <= 0:
+        step_kv = sum(wl_mod.algorithmic_bytes(wl_mod.workload_ctx_lens(wl), sp.num_q_heads,
+                                               sp.num_kv_heads, sp.head_dim, wl.page_size,
+                                               sp.window, k_eq_v=args.k_eq_v, sink=args.sink,
+                                               q_len=args.q_len) for sp in wl.layers.values())
+        copies = int(min(256, max(2, -(-(768 << 20) // step_kv))))
     t_gen = time.time()
     layers = []
     for kind in ("global", "sliding"):
@@ -138,7 +149,7 @@ def main() -> int:
         k0 = bf(inp.k_pool)
         v0 = k0 if args.k_eq_v else bf(inp.v_pool)
         ks, vs = [k0], [v0]
-        for _ in range(1, max(1, args.copies)):
+        for _ in range(1, copies):
             ks.append(k0.clone())
             vs.append(ks[-1] if args.k_eq_v else v0.clone())
         plan = pda.decode_attn_plan(d["B"], d["Hq"], d["Hkv"], d["D"], d["S"], d["M"], d["P"],
@@ -225,16 +236,33 @@ def main() -> int:
     ms_per_step = (t1 - t0) * 1e3 / K
 
     # Per-layer breakdown, after (outside) the timed region: events around each layer call.
-    detail = {}
-    for L in layers:
+    # Cold: before every call a 512 MB buffer is written (outside the event pair), which evicts
+    # the L2s and the MALL, so the call reads its K/V from HBM whatever the workload's size.
+    # Hot (a diagnostic): the same call on the same pool copy back to back, so a layer small
+    # enough to stay in the L2s and the MALL shows it (GB/s above the HBM peak). Fills queued in
+    # front keep the GPU busy while the host enqueues the calls, so short calls are not timed
+    # waiting for the host.
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def timed_calls(L, n, flush):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(min(K, 20))]
+               for _ in range(n)]
+        if not flush:
+            for i in range(8):
+                flush_buf.fill_(i)
         for i, (ea, eb) in enumerate(evs):
+            if flush:
+                flush_buf.fill_(i & 0xFF)
             ea.record(stream)
-            run_layer(L, i % R)
+            run_layer(L, i % R if flush else 0)
             eb.record(stream)
         torch.cuda.synchronize()
-        us = sorted(1e3 * ea.elapsed_time(eb) for ea, eb in evs)
+        return sorted(1e3 * ea.elapsed_time(eb) for ea, eb in evs)
+
+    detail = {}
+    for L in layers:
+        us = timed_calls(L, 20, flush=True)
+        hot = timed_calls(L, 20, flush=False)
         med = us[len(us) // 2]
         if args.append:
             eva = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -249,6 +277,7 @@ def main() -> int:
         detail[L["kind"]] = {"us_per_call_median": round(med, 2),
                              "us_per_call_p10": round(us[len(us) // 10], 2),
                              "us_per_call_p90": round(us[(9 * len(us)) // 10], 2),
+                             "hot_us_per_call_median": round(hot[len(hot) // 2], 2),
                              "GB_per_s": round(L["bytes"] / (med * 1e-6) / 1e9, 1),
                              "pct_of_hbm_peak": round(100 * L["bytes"] / (med * 1e-6) / 1e9 /
                                                       PEAK_HBM_GBS, 2)}

@@ -74,8 +74,8 @@ def _global(hq: int, hkv: int, q_mult: float = 1.0) -> LayerSpec:
     return LayerSpec("global", hq, hkv, 512, 0, q_mult)
 
 
-def _sliding(q_mult: float = 1.0) -> LayerSpec:
-    return LayerSpec("sliding", 16, 8, 256, 1024, q_mult)
+def _sliding(hq: int = 16, hkv: int = 8, q_mult: float = 1.0) -> LayerSpec:
+    return LayerSpec("sliding", hq, hkv, 256, 1024, q_mult)
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -100,6 +100,17 @@ WORKLOADS: Dict[str, Workload] = {
     "very_long_b2": Workload(
         "very_long_b2", 5, 2, [65536 + 1024] * 2, {"global": _global(16, 2)}, num_pages=16384,
         description="batch 2, ctx 66560, global 16/2 heads D 512, 16384-page pool"),
+    # One GPU's share under 2-way tensor parallelism over KV heads: each GPU holds half the KV
+    # heads, their query heads and their own pools; attention itself needs no exchange.
+    "long_ctx_tp2": Workload(
+        "long_ctx_tp2", 6, 4, [32768 + 1024] * 4,
+        {"global": _global(8, 1, q_mult=2.0), "sliding": _sliding(8, 4, q_mult=2.0)},
+        description="one GPU's share of long_ctx at 2-way KV-head tensor parallelism: batch 4, "
+                    "ctx 33792; global 8/1 heads D 512 and sliding 8/4 heads D 256 W 1024"),
+    "very_long_b1_tp2": Workload(
+        "very_long_b1_tp2", 7, 1, [131072 + 1024], {"global": _global(8, 1)}, num_pages=16384,
+        description="one GPU's share of very_long_b1 at 2-way KV-head tensor parallelism: "
+                    "batch 1, ctx 132096, global 8/1 heads D 512, 16384-page pool"),
 }
 
 

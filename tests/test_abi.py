@@ -80,6 +80,10 @@ def expected_workspace(B, Hq, ns, D, L=1):
           q_len=8), 64),                                              # G 4: capped by tiles
     (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024), 64),
     (dict(batch=1, max_pages_per_seq=4, max_ctx_len=64), 4),          # capped: >= 1 tile/split
+    (dict(num_q_heads=8, num_kv_heads=1), 64),                        # TP2 share of 4 x 33792
+    (dict(num_q_heads=8, num_kv_heads=4, head_dim=256, window=1024), 32),  # its sliding layer
+    (dict(batch=1, num_q_heads=8, num_kv_heads=1, max_pages_per_seq=8256, num_pages=16384,
+          max_ctx_len=132096), 256),                                  # TP2 share of 1 x 132096
 ])
 def test_plan_split_counts(kw, splits):
     p = plan(**kw)
