@@ -1,8 +1,8 @@
 /*
  * decode_attn.h — C ABI of the paged GQA split-KV decode-attention library for MI355X (gfx950).
  *
- * What it computes. Decode attention (one new query token per sequence, or up to 16 causal ones)
- * over a paged KV cache for the two layer kinds of a Gemma-4-style model: "global" layers (every cached key attended; head_dim 512 in Gemma 4) and
+ * What it computes. Decode attention (one new query token per sequence, or up to 8192 causal ones:
+ * speculative verification and chunked prefill) over a paged KV cache for the two layer kinds of a Gemma-4-style model: "global" layers (every cached key attended; head_dim 512 in Gemma 4) and
  * "sliding-window" layers (only the last W keys attended; head_dim 256 in Gemma 4). The layer kinds
  * may differ in head dim, KV-head count and window (Sparse-vLLM PR #27 "feat: support Gemma 4 and
  * native multimodal inference", section "Gemma 4 文本推理" / Gemma 4 text inference). Several query
@@ -23,12 +23,15 @@
  * gives out = 0 and lse = -inf. The sink keys give the StreamingLLM-style views the same page
  * supports (section "Gemma 4 文本推理"): a window of recent keys plus a few leading ones. L > 1
  * is causal multi-token verification (the last L cached keys are the new tokens themselves; vLLM
- * learning notes, the MLA backend notes on causal multi-token verification); L = 1 is the
- * single-token decode that section "核心操作" of the same notes describes.
+ * learning notes, the MLA backend notes on causal multi-token verification) or a chunk of a
+ * prompt's prefill over the paged cache; L = 1 is the single-token decode. Section "核心操作" of
+ * the same notes names both operations an attention layer serves: prefill and decode.
  *
  * How. Split-KV: stage 1 cuts each sequence's key range into num_splits chunks and writes, per
  * (b, i, h, split), the chunk's normalised partial output and its log-sum-exp; stage 2 merges the
- * partials of each (b, i, h) by their log-sum-exps. The partial buffer reserves one LSE value per
+ * partials of each (b, i, h) by their log-sum-exps. With one chunk (num_splits = 1, the planner's
+ * pick when the query blocks alone fill the GPU, as in prefill) the partial is the result: stage 1
+ * then writes out and lse_out directly and stage 2 is not launched. The partial buffer reserves one LSE value per
  * (b, i, h, split) next to the D partial outputs and is sized once, for the worst case, so that no
  * call allocates and calls can be captured in a HIP graph (vLLM learning notes, section
  * "MLA 与 Sparse MLA（DSA）", split-KV MLA decode). A plan is computed on the host from the shape
@@ -89,7 +92,7 @@ typedef enum {
 
 /* Compiled kernel variants. */
 #define DECODE_ATTN_MAX_SPLITS_LIMIT 1024 /* hard upper bound on num_splits */
-#define DECODE_ATTN_MAX_Q_LEN 16          /* most query tokens per sequence in one call */
+#define DECODE_ATTN_MAX_Q_LEN 8192        /* most query tokens per sequence in one call */
 
 /* The shape a plan covers. Values are upper bounds for the calls made with the plan. */
 typedef struct {
@@ -112,8 +115,8 @@ typedef struct {
                                 sequence (attention sinks of StreamingLLM-style views); 0 = none.
                                 Ignored when window == 0, where every key is attended anyway */
   int32_t q_len;             /* L: new query tokens per sequence, 0 or 1 = single-token decode,
-                                up to DECODE_ATTN_MAX_Q_LEN (speculative verification, short
-                                chunks); every call with the plan passes L tokens per sequence */
+                                up to DECODE_ATTN_MAX_Q_LEN (speculative verification, chunked
+                                prefill); every call with the plan passes L tokens per sequence */
 } decode_attn_problem;
 
 /* A plan: plain data, copy it freely; there is nothing to free. */
@@ -147,7 +150,7 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
 
 /*
  * decode_attn_global — attention of a global layer (plan->problem.window == 0): stage 1 then
- * stage 2 on `stream`. `batch` (0 <= batch <= plan->problem.batch) sequences are computed; batch 0
+ * stage 2 on `stream` (stage 1 alone, writing out and lse_out, when plan->num_splits == 1). `batch` (0 <= batch <= plan->problem.batch) sequences are computed; batch 0
  * returns DECODE_ATTN_OK without launching. `scale` multiplies q.k (1/sqrt(D) for Gemma-style
  * layers). lse_out may be NULL. workspace must hold plan->workspace_bytes. A plan made with
  * values_are_keys = 1 requires v_pool == k_pool (else DECODE_ATTN_ERR_SHAPE); the same pool passed
@@ -220,8 +223,9 @@ int decode_attn_append_kv(const decode_attn_plan_t* plan, const void* k_new, con
 const char* decode_attn_status_str(int status);
 
 /* Library version, major * 10000 + minor * 100 + patch. The minor number changes with the layout
- * of decode_attn_problem / decode_attn_plan_t (0.2: sink and q_len fields). */
-#define DECODE_ATTN_VERSION 200
+ * of decode_attn_problem / decode_attn_plan_t (0.2: sink and q_len fields); 0.2.1: q_len up to
+ * 8192, one-split calls without stage 2. */
+#define DECODE_ATTN_VERSION 201
 int decode_attn_version(void);
 
 #ifdef __cplusplus

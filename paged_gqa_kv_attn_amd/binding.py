@@ -74,7 +74,7 @@ def library_path() -> str:
 
 
 # decode_attn_version() of the library whose struct layouts Problem and Plan mirror.
-ABI_VERSION = 200
+ABI_VERSION = 201
 
 
 def load_library():

@@ -109,9 +109,11 @@ int check_stage2_args(const decode_attn_plan_t* plan, int32_t batch, const void*
   return DECODE_ATTN_OK;
 }
 
+// Stage 1 writing its partials to o_part / lse_part ([B, L, Hq, num_splits, D] and
+// [B, L, Hq, num_splits] fp32).
 int run_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
                const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
-               int32_t batch, float scale, void* workspace, hipStream_t stream) {
+               int32_t batch, float scale, float* o_part, float* lse_part, hipStream_t stream) {
   const decode_attn_problem& p = plan->problem;
   Stage1Args a;
   a.q = static_cast<const uint16_t*>(q);
@@ -119,8 +121,8 @@ int run_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool
   a.v_pool = static_cast<const uint16_t*>(v_pool);
   a.block_table = block_table;
   a.ctx_lens = ctx_lens;
-  a.o_part = static_cast<float*>(workspace);
-  a.lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->partial_lse_offset);
+  a.o_part = o_part;
+  a.lse_part = lse_part;
   a.num_q_heads = p.num_q_heads;
   a.num_kv_heads = p.num_kv_heads;
   a.page_size = p.page_size;
@@ -166,7 +168,16 @@ int attend(const decode_attn_plan_t* plan, int expected_kind, const void* q, con
   rc = check_stage2_args(plan, batch, workspace, workspace_bytes, out, lse_out);
   if (rc != DECODE_ATTN_OK || batch == 0) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, workspace, s);
+  float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->partial_lse_offset);
+  if (plan->num_splits == 1) {
+    // One chunk per row: its normalised output and log-sum-exp already are the result, and the
+    // partial planes [B, L, Hq, 1, D] / [B, L, Hq, 1] have the layout of out / lse_out, so stage 1
+    // writes them in place and the merge is skipped.
+    return run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, out,
+                      lse_out != nullptr ? lse_out : lse_ws, s);
+  }
+  rc = run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale,
+                  static_cast<float*>(workspace), lse_ws, s);
   if (rc != DECODE_ATTN_OK) return rc;
   return run_stage2(plan, batch, workspace, out, lse_out, s);
 }
@@ -272,7 +283,10 @@ int decode_attn_stage1(const decode_attn_plan_t* plan, const void* q, const void
   rc = check_stage1_args(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, workspace,
                          workspace_bytes);
   if (rc != DECODE_ATTN_OK || batch == 0) return rc;
-  return run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, workspace,
+  return run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale,
+                    static_cast<float*>(workspace),
+                    reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                             plan->partial_lse_offset),
                     static_cast<hipStream_t>(stream));
 }
 

@@ -80,6 +80,10 @@ def expected_workspace(B, Hq, ns, D, L=1):
           q_len=8), 64),                                              # G 4: capped by tiles
     (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024), 64),
     (dict(batch=1, max_pages_per_seq=4, max_ctx_len=64), 4),          # capped: >= 1 tile/split
+    (dict(q_len=16), 16),                                             # 4 blocks of 4 queries
+    (dict(q_len=512), 1),                                             # prefill chunk: 128 blocks
+    (dict(batch=1, q_len=64, max_ctx_len=4096), 16),                  # 16 blocks, 256 tiles
+    (dict(batch=1, num_kv_heads=8, head_dim=256, window=1024, q_len=256), 4),  # 8 x 16 blocks
     (dict(num_q_heads=8, num_kv_heads=1), 64),                        # TP2 share of 4 x 33792
     (dict(num_q_heads=8, num_kv_heads=4, head_dim=256, window=1024), 32),  # its sliding layer
     (dict(batch=1, num_q_heads=8, num_kv_heads=1, max_pages_per_seq=8256, num_pages=16384,
@@ -134,7 +138,7 @@ def test_plan_force_and_cap():
     (dict(window=-1), ERR_SHAPE),
     (dict(window=64, sink=-1), ERR_SHAPE),
     (dict(q_len=-1), ERR_SHAPE),
-    (dict(q_len=17), ERR_SHAPE),
+    (dict(q_len=8193), ERR_SHAPE),
     (dict(batch=4096, q_len=16), ERR_SHAPE),     # 65536 (sequence, token) pairs
     (dict(force_splits=1025), ERR_SHAPE),
     (dict(max_splits=2000), ERR_SHAPE),
@@ -239,7 +243,7 @@ def test_status_strings(lib):
     for code in range(8):
         assert binding.decode_attn_status_str(code).startswith(binding.STATUS_NAMES[code])
     assert "unknown" in binding.decode_attn_status_str(99)
-    assert binding.decode_attn_version() == binding.ABI_VERSION == 200
+    assert binding.decode_attn_version() == binding.ABI_VERSION == 201
 
 
 def test_binding_rejects_tensors_smaller_than_the_plan():
