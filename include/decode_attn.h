@@ -178,8 +178,8 @@ int decode_attn_sliding(const decode_attn_plan_t* plan, const void* q, const voi
  * Writes the workspace, which holds two planes:
  *     o_part [B, L, Hq, num_splits, D] fp32 at byte offset 0
  *     lse    [B, L, Hq, num_splits]    fp32 at byte offset plan->partial_lse_offset
- * The queries of a sequence are taken in blocks of 16 / G, or 32 / G when G * L > 16 (one
- * block when L = 1). Split s of a
+ * The queries of a sequence are taken in blocks of 16 / G, 32 / G when G * L > 16, or 64 / G
+ * when G * L >= 64 (one block when L = 1). Split s of a
  * block covers the tiles [floor(s*T/ns), floor((s+1)*T/ns)) of the block's list of T 16-key
  * tiles (ns = num_splits). With lo and n those of the block's first and last query respectively,
  * the list holds the tiles 0 .. ceil(k/16) - 1 that overlap the sink keys [0, k), k = min(sink,

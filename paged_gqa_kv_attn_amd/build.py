@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdecode_attn.so")
-SOURCES = ["decode_attn.cpp", "stage1.hip", "stage2.hip", "append.hip"]
+SOURCES = ["decode_attn.cpp", "stage1.hip", "prefill.hip", "stage2.hip", "append.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU instructions are kept out of the generated code.
@@ -29,9 +29,16 @@ def _hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
+# Per-source flags. The prefill kernel keeps its MFMA accumulators in ordinary VGPRs: with the
+# default heuristics the score and output accumulators both claim AGPRs and the compiler moves the
+# output block between the two register files on every loop step.
+SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, extra=()) -> str:
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc()] + COMMON_FLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([_hipcc()] + COMMON_FLAGS + SOURCE_FLAGS.get(src, []) + list(extra) +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -134,8 +134,10 @@ int run_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool
   a.num_qblocks = qblocks_of(p, plan->group_size);
   a.num_splits = plan->num_splits;
   a.scale_log2 = scale * 1.442695040888963407360f;
-  if (launch_stage1(a, p.head_dim, plan->group_size, batch, stream) != hipSuccess)
-    return DECODE_ATTN_ERR_HIP;
+  const hipError_t err = stage1_use_prefill(plan->group_size, a.q_len)
+                             ? launch_prefill(a, p.head_dim, plan->group_size, batch, stream)
+                             : launch_stage1(a, p.head_dim, plan->group_size, batch, stream);
+  if (err != hipSuccess) return DECODE_ATTN_ERR_HIP;
   return DECODE_ATTN_OK;
 }
 
@@ -232,8 +234,12 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   // Blocks with two row groups (G * q_len > 16) do twice the MFMA and softmax work per tile and
   // likewise run best at two per CU (measured: 4 tokens on the 32K global layer 131 -> 113 us).
   const bool two_row_groups = stage1_row_groups(G, p.q_len) == 2;
-  const int64_t target =
-      ((p.head_dim >= 512 && !p.values_are_keys && !two_row_groups) ? 1 : 2) * (int64_t)p.num_cus;
+  // Prefill blocks (64 rows, K/V tiles staged in LDS) fit one workgroup per CU at head_dim 512
+  // (133 KB of LDS) and two at 256.
+  const bool one_per_cu = stage1_use_prefill(G, p.q_len)
+                              ? p.head_dim >= 512
+                              : (p.head_dim >= 512 && !p.values_are_keys && !two_row_groups);
+  const int64_t target = (one_per_cu ? 1 : 2) * (int64_t)p.num_cus;
   int64_t splits = (target + pairs - 1) / pairs;
   int64_t cap = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
   if (cap > p.max_splits) cap = p.max_splits;

@@ -12,6 +12,7 @@ constexpr int kTile = 16;                     // keys per tile: the M dimension 
 constexpr int kDefaultMaxSplits = 256;
 constexpr int kMinTilesPerSplit = 1;          // a chunk holds one 16-key tile at least
 constexpr int kStage2Threads = 256;
+constexpr int kPrefillRows = 64;              // (query, head) rows of a prefill workgroup
 
 // Kernel arguments of stage 1 (one workgroup per (split, query block, kv head, sequence)).
 struct Stage1Args {
@@ -68,6 +69,9 @@ struct AppendArgs {
 hipError_t launch_stage1(const Stage1Args& args, int head_dim, int group_size, int batch,
                          hipStream_t stream);
 hipError_t launch_stage2(const Stage2Args& args, int batch, hipStream_t stream);
+// Stage 1 for long query chunks (prefill.hip): the same arguments and outputs, 64-row blocks.
+hipError_t launch_prefill(const Stage1Args& args, int head_dim, int group_size, int batch,
+                          hipStream_t stream);
 hipError_t launch_append(const AppendArgs& args, int batch, hipStream_t stream);
 
 // True when a stage-1 kernel is compiled for (head_dim, group_size).
@@ -79,8 +83,14 @@ inline int stage1_row_groups(int group_size, int q_len) {
   return (q_len > 1 && group_size * q_len > 16) ? 2 : 1;
 }
 
+// Long query chunks (G * q_len >= 64 rows per kv head) run on the prefill kernel.
+inline bool stage1_use_prefill(int group_size, int q_len) {
+  return q_len > 1 && group_size * q_len >= kPrefillRows;
+}
+
 // Queries one stage-1 workgroup serves, and the query blocks of one (sequence, kv head).
 inline int stage1_block_queries(int group_size, int q_len) {
+  if (stage1_use_prefill(group_size, q_len)) return kPrefillRows / group_size;
   return 16 * stage1_row_groups(group_size, q_len) / group_size;
 }
 inline int stage1_query_blocks(int group_size, int q_len) {

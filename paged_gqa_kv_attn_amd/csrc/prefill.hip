@@ -1,0 +1,481 @@
+// prefill.hip — stage 1 for long query chunks (prefill over the paged cache).
+//
+// The operation is stage 1's (decode_attn_stage1 in decode_attn.h): for query token i of
+// sequence b at position n - L + i, query head h, the softmax of scale * q.k over the keys the
+// query attends inside this split's share of the block's tile list, written as a normalised
+// partial output and its log-sum-exp. Prefill is the attention layer's other operation next to
+// decode (vLLM learning notes "模型库与算子层 — 概念", section "核心操作"); the partial format and the
+// merge are the split-KV ones of section "MLA 与 Sparse MLA（DSA）" of the same notes.
+//
+// What changes against the decode kernel is the shape of the work. Decode has 16-32 (query,
+// head) rows per KV head and streams K/V once, so the decode kernel splits the head dim across
+// its waves and is bound by HBM. A prefill chunk has thousands of rows per KV head, and every
+// K/V tile serves all of them: the work is MFMA-bound. Here a workgroup owns 64 rows (16 per
+// wave, each wave with the full head dim), all waves share one 32-key K/V tile staged in LDS,
+// and no scores cross waves:
+//
+//   - K/V tile of the step (32 keys = two 16-key entries of the tile list, each on its own page)
+//     in LDS, double-buffered; the next tile is fetched into registers during the step and
+//     written to the other buffer at its end (one barrier per step). Rows are padded by 16 bytes
+//     and 16-byte chunks are XOR-swizzled within 64-byte groups, so the score operand reads (16
+//     keys, same column) and the P.V operand reads (16 column groups, same key) are free of
+//     bank conflicts.
+//   - scores: S^T[32 keys][16 rows] per wave with v_mfma_f32_16x16x32_bf16, A = K (keys x 32
+//     columns, from LDS), B = the wave's q rows (in registers for the whole kernel);
+//   - online softmax per row in base 2, exactly as the decode kernel (masks by select, running
+//     max and sum, accumulator rescaled only when a max moved);
+//   - P.V with v_mfma_f32_16x16x32_bf16: A = P (16 rows x 32 keys) straight from the score
+//     registers; the 32 keys of the MFMA's reduction run in the order the score layout leaves
+//     them (keys 4g..4g+3 then 16+4g..16+4g+3 for lane group g), and B = V takes its keys in that
+//     same order; lane n owns output columns [n*D/16, (n+1)*D/16), so each B read is 16
+//     contiguous bytes of one key row, transposed in the lane with v_perm_b32.
+//
+// Keys outside the union of the block's ranges (and entries past the split) are written to LDS as
+// zeros, so 0 * NaN never reaches P.V; per-row causal, window and sink masks are applied to the
+// scores.
+
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace decode_attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStepKeys = 2 * kTile;  // two tile-list entries per loop step
+constexpr float kLn2 = 0.693147180559945309417f;
+
+template <int D>
+struct PShape {
+  static_assert(D == 256 || D == 512, "head_dim");
+  static constexpr int kPitch = D + 8;                      // LDS row pitch, bf16
+  static constexpr int kChunks = D / 8;                     // 16-byte chunks per key row
+  static constexpr int kSwz = D / 128 - 1;                  // chunk swizzle mask
+  static constexpr int kQSteps = D / 32;                    // score MFMAs per 16 keys
+  static constexpr int kLaneCols = D / 16;                  // output columns per lane
+  static constexpr int kVGroups = kLaneCols / 8;            // 8-column groups per lane
+  static constexpr int kLoads = kStepKeys * kChunks / kThreads;  // 16-B loads per thread per matrix
+  static constexpr int kKeysPerPass = kThreads / kChunks;   // key rows one pass of loads covers
+};
+
+// Physical position of 16-byte chunk c inside a key row: chunks are XOR-swizzled inside each
+// group of 4 (D = 512) or 2 (D = 256) by the index of their 64-column (128-byte) block, which
+// spreads the 16 lanes reading column group n of one key row over all 64 banks.
+template <int D>
+__device__ __forceinline__ int swz(int c) {
+  return c ^ ((c >> 4) & PShape<D>::kSwz);
+}
+
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int32_t load_uniform(const int32_t* p, size_t idx) {
+  return ((const_i32_ptr)(p))[idx];
+}
+
+__device__ __forceinline__ float max_xor16_32(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const float m16 = fmaxf(__builtin_bit_cast(float, (uint32_t)r16[0]),
+                          __builtin_bit_cast(float, (uint32_t)r16[1]));
+  const uint32_t c = __builtin_bit_cast(uint32_t, m16);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r32[0]),
+               __builtin_bit_cast(float, (uint32_t)r32[1]));
+}
+
+__device__ __forceinline__ float sum_xor16_32(float v) {
+  const uint32_t b = __builtin_bit_cast(uint32_t, v);
+  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const float s16 = __builtin_bit_cast(float, (uint32_t)r16[0]) +
+                    __builtin_bit_cast(float, (uint32_t)r16[1]);
+  const uint32_t c = __builtin_bit_cast(uint32_t, s16);
+  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r32[0]) + __builtin_bit_cast(float, (uint32_t)r32[1]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// SHARED: the pools are one buffer (values are the keys); the V tile is the K tile.
+template <int D, int G, bool SHARED>
+__global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
+  using Sh = PShape<D>;
+  constexpr int kMats = SHARED ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][kMats][kStepKeys][Sh::kPitch];
+
+  constexpr int kQB = kPrefillRows / G;  // queries per block
+  const int ns = a.num_splits;
+  const int split = (int)blockIdx.x % ns;
+  // Later queries attend more keys: blocks are numbered from the last one so the longest
+  // workgroups are dispatched first.
+  const int qb = a.num_qblocks - 1 - (int)blockIdx.x / ns;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = lane >> 4;
+  const int col = lane & 15;
+  const int S = a.page_size;
+  const int L = a.q_len;
+  const int sink = a.sink;
+
+  // Row r of the block (0..63) is query qb * kQB + r / G, head kvh * G + r % G. This wave owns
+  // rows 16 * wave .. + 15; lane (col, grp) scores for row 16 * wave + col.
+  auto row_query = [&](int r) { return qb * kQB + r / G; };
+  auto row_valid = [&](int r) { return row_query(r) < L; };
+  auto out_row = [&](int r) -> size_t {
+    return ((size_t)b * L + row_query(r)) * a.num_q_heads + (size_t)kvh * G + r % G;
+  };
+
+  const int max_keys = a.max_pages_per_seq * S;
+  int n_ctx = load_uniform(a.ctx_lens, b);
+  n_ctx = n_ctx < 0 ? 0 : (n_ctx > max_keys ? max_keys : n_ctx);
+  auto query_end = [&](int i) { const int e = n_ctx - L + i + 1; return e < 0 ? 0 : e; };
+  auto window_lo = [&](int e) { return (a.window > 0 && e > a.window) ? e - a.window : 0; };
+  const int q_last = (qb + 1) * kQB < L ? (qb + 1) * kQB - 1 : L - 1;
+  const int n = query_end(q_last);             // union of the block's ranges: [lo, n) + sinks
+  const int lo = window_lo(query_end(qb * kQB));
+  const int sk = sink < lo ? sink : lo;
+  const int my_row = 16 * wave + col;
+  const int row_n = row_valid(my_row) ? query_end(row_query(my_row)) : 0;
+  const int row_lo = window_lo(row_n);
+
+  // Tile list (as in the decode kernel): sink tiles 0 .. st-1, then the window's tiles from
+  // physical tile w0 on; this split takes entries [t_begin, t_end).
+  const int st = (sk + kTile - 1) / kTile;
+  const int w0 = st > lo / kTile ? st : lo / kTile;
+  const int tile_hi = (n + kTile - 1) / kTile;
+  const int T = st + (tile_hi > w0 ? tile_hi - w0 : 0);
+  const int shift = w0 - st;
+  const int t_begin = (int)(((int64_t)split * T) / ns);
+  const int t_end = (int)(((int64_t)(split + 1) * T) / ns);
+  const int tiles_per_page = S / kTile;
+  auto phys_tile = [&](int v) { return v >= st ? v + shift : v; };
+  const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
+
+  if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
+    for (int idx = tid; idx < kPrefillRows * D; idx += kThreads) {
+      const int r = idx / D;
+      if (row_valid(r)) a.o_part[(out_row(r) * ns + split) * D + (idx - r * D)] = 0.f;
+    }
+    if (tid < kPrefillRows && row_valid(tid)) a.lse_part[out_row(tid) * ns + split] = -INFINITY;
+    return;
+  }
+  const int t_last = t_end - 1;
+
+  // q rows of this wave as the B operand of the score MFMA: lane (col, grp) holds row
+  // 16 * wave + col, columns 32 * c + 8 * grp .. + 7 (zero past the last query).
+  bf16x8 qop[Sh::kQSteps];
+  {
+    const bool rv = row_valid(my_row);
+    const uint16_t* qr = a.q + out_row(rv ? my_row : my_row % G) * D;  // block's first query
+#pragma unroll
+    for (int c = 0; c < Sh::kQSteps; ++c) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qr + 32 * c + 8 * grp);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qop[c] = __builtin_bit_cast(bf16x8, rv ? v : z);
+    }
+  }
+
+  // Staging of one step's tile (list entries e, e + 1): thread tid loads chunks
+  // tid + kThreads * k, i.e. key row k * kKeysPerPass + tid / kChunks, chunk tid % kChunks. The
+  // first kLoads / 2 loads are entry e's, the rest entry e + 1's; a thread's byte offsets inside
+  // a tile are the same every step, so each load is a uniform tile address plus a fixed offset.
+  const int ld_key0 = tid / Sh::kChunks;
+  const int ld_chunk = tid % Sh::kChunks;
+  constexpr int kHalf = Sh::kLoads / 2;
+  auto ld_key = [&](int k) { return k * Sh::kKeysPerPass + ld_key0; };
+  uint32_t ld_off[Sh::kLoads];
+#pragma unroll
+  for (int k = 0; k < Sh::kLoads; ++k)
+    ld_off[k] = (uint32_t)(((ld_key(k) % kTile) * D + 8 * ld_chunk) * 2);
+  u32x4 stk[Sh::kLoads];
+  u32x4 stv[SHARED ? 1 : Sh::kLoads];
+  // Element offset of entry v's tile (page id pid) in a pool, and whether its page is valid.
+  auto entry_base = [&](int v, int pid, bool& page_ok) -> size_t {
+    const int pc = phys_tile(v < t_end ? v : t_last);
+    page_ok = (unsigned)pid < (unsigned)a.num_pages;
+    const int pg = page_ok ? pid : 0;
+    const int within = pc - (pc / tiles_per_page) * tiles_per_page;
+    return (((size_t)pg * a.num_kv_heads + kvh) * S + within * kTile) * D;
+  };
+  auto entry_pid = [&](int v) -> int32_t {
+    const int pc = phys_tile(v < t_end ? v : t_last);
+    return load_uniform(table_row, pc / tiles_per_page);
+  };
+  // Page ids of entries e, e + 1 as a vector (lane u holds entry e + (u & 1)), fetched a step
+  // ahead and read back with v_readlane.
+  auto pid_vector = [&](int e) -> int32_t {
+    const int v = e + (lane & 1);
+    const int pc = phys_tile(v < t_end ? v : t_last);
+    return table_row[pc / tiles_per_page];
+  };
+  auto issue_loads = [&](int e, int pid0, int pid1, bool* page_ok) {
+    const size_t base0 = entry_base(e, pid0, page_ok[0]);
+    const size_t base1 = entry_base(e + 1, pid1, page_ok[1]);
+    const char* k0 = reinterpret_cast<const char*>(a.k_pool + base0);
+    const char* k1 = reinterpret_cast<const char*>(a.k_pool + base1);
+    const char* v0 = reinterpret_cast<const char*>(a.v_pool + base0);
+    const char* v1 = reinterpret_cast<const char*>(a.v_pool + base1);
+#pragma unroll
+    for (int k = 0; k < Sh::kLoads; ++k) {
+      stk[k] = *reinterpret_cast<const u32x4*>((k < kHalf ? k0 : k1) + ld_off[k]);
+      if constexpr (!SHARED)
+        stv[k] = *reinterpret_cast<const u32x4*>((k < kHalf ? v0 : v1) + ld_off[k]);
+    }
+  };
+  // Key t of entry v is in the union of the block's ranges (read at all) iff its page is valid,
+  // v < t_end, t < n and (t >= lo or t < sk). An entry is full when all its 16 keys are.
+  auto entry_full = [&](int v, bool page_ok) {
+    const int t0 = phys_tile(v < t_end ? v : t_last) * kTile;
+    return (v < t_end) && page_ok && t0 + kTile <= n && (t0 >= lo || t0 + kTile <= sk);
+  };
+  // Stores the staged tile; keys outside the union are then overwritten with zeros (only entries
+  // at the edges of the ranges, or of invalid pages, have any). Returns whether both are full.
+  auto store_tile = [&](int buf, int e, const bool* page_ok) -> bool {
+#pragma unroll
+    for (int k = 0; k < Sh::kLoads; ++k) {
+      *reinterpret_cast<u32x4*>(&kv_lds[buf][0][ld_key(k)][8 * swz<D>(ld_chunk)]) = stk[k];
+      if constexpr (!SHARED)
+        *reinterpret_cast<u32x4*>(&kv_lds[buf][1][ld_key(k)][8 * swz<D>(ld_chunk)]) = stv[k];
+    }
+    const bool full = entry_full(e, page_ok[0]) && entry_full(e + 1, page_ok[1]);
+    if (!full) {
+#pragma unroll
+      for (int k = 0; k < Sh::kLoads; ++k) {
+        const int key = ld_key(k);
+        const int v = e + (k < kHalf ? 0 : 1);
+        const int t = phys_tile(v < t_end ? v : t_last) * kTile + key % kTile;
+        const bool in = (v < t_end) & page_ok[k < kHalf ? 0 : 1] & (t < n) & ((t >= lo) | (t < sk));
+        if (!in) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&kv_lds[buf][0][key][8 * swz<D>(ld_chunk)]) = z;
+          if constexpr (!SHARED)
+            *reinterpret_cast<u32x4*>(&kv_lds[buf][1][key][8 * swz<D>(ld_chunk)]) = z;
+        }
+      }
+    }
+    return full;
+  };
+
+  // Rows of this wave that exist attend every key in [wave_lo, wave_n) (sinks aside): a step whose
+  // keys all lie there, in two full entries, needs no per-row mask.
+  int wave_n = row_valid(my_row) ? row_n : INT32_MAX;
+  int wave_lo = row_valid(my_row) ? row_lo : 0;
+#pragma unroll
+  for (int x = 1; x < 16; x <<= 1) {
+    wave_n = min(wave_n, __shfl_xor(wave_n, x));
+    wave_lo = max(wave_lo, __shfl_xor(wave_lo, x));
+  }
+  wave_n = __builtin_amdgcn_readfirstlane(wave_n);
+  wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
+
+  // Prologue: tile of step 0 into LDS buffer 0, the tile of step 1 in flight.
+  bool ok_cur[2], ok_next[2];
+  issue_loads(t_begin, entry_pid(t_begin), entry_pid(t_begin + 1), ok_next);
+  int32_t pid_next = pid_vector(t_begin + 2);
+  bool full_cur = store_tile(0, t_begin, ok_next);
+  ok_cur[0] = ok_next[0];
+  ok_cur[1] = ok_next[1];
+  issue_loads(t_begin + 2, __builtin_amdgcn_readlane(pid_next, 0),
+              __builtin_amdgcn_readlane(pid_next, 1), ok_next);
+  pid_next = pid_vector(t_begin + 4);
+  __syncthreads();
+
+  float m_run = -INFINITY;  // running max (base 2) of row my_row
+  float l_run = 0.f;        // running sum of exp2(s - m_run)
+  f32x4 acc[Sh::kLaneCols];  // O[rows 16 * wave + 4 * grp + i][col * kLaneCols + e] = acc[e][i]
+#pragma unroll
+  for (int e = 0; e < Sh::kLaneCols; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int buf = 0;
+  for (int e0 = t_begin; e0 < t_end; e0 += 2) {
+    // Scores S^T for the two entries: lane (col, grp) gets keys 4 * grp + i of entry e0 + g
+    // for row my_row.
+    f32x4 sc[2];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < Sh::kQSteps; c += 2) {
+        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(
+            &kv_lds[buf][0][kTile * g + col][8 * swz<D>(4 * c + grp)]);
+        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(
+            &kv_lds[buf][0][kTile * g + col][8 * swz<D>(4 * (c + 1) + grp)]);
+        p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[c], p0, 0, 0, 0);
+        p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[c + 1], p1, 0, 0, 0);
+      }
+      sc[g] = p0 + p1;
+    }
+
+    // Masks and online softmax of row my_row over the 32 keys.
+    float s2[2][4];
+    float mt = -INFINITY;
+    const int ta = phys_tile(e0 < t_end ? e0 : t_last) * kTile;
+    const int tb = phys_tile(e0 + 1 < t_end ? e0 + 1 : t_last) * kTile;
+    const bool unmasked = full_cur && (ta > tb ? ta : tb) + kTile <= wave_n &&
+                          (ta >= wave_lo || ta + kTile <= sink) &&
+                          (tb >= wave_lo || tb + kTile <= sink);
+    if (unmasked) {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s2[g][i] = sc[g][i] * a.scale_log2;
+          mt = fmaxf(mt, s2[g][i]);
+        }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int v = e0 + g;
+        const int t0 = (g == 0 ? ta : tb) + 4 * grp;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + i;
+          const bool att = (v < t_end) & ok_cur[g] & (t < row_n) & ((t >= row_lo) | (t < sink));
+          s2[g][i] = att ? sc[g][i] * a.scale_log2 : -INFINITY;
+          mt = fmaxf(mt, s2[g][i]);
+        }
+      }
+    }
+    mt = max_xor16_32(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float p[2][4];
+    float ps = 0.f;
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[g][i] = __builtin_amdgcn_exp2f(s2[g][i] - m_use);
+        ps += p[g][i];
+      }
+    ps = sum_xor16_32(ps);
+    l_run = l_run * alpha + ps;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+      float al[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * grp + i);
+#pragma unroll
+      for (int e = 0; e < Sh::kLaneCols; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[e][i] *= al[i];
+    }
+    // P as the A operand: row my_row, reduction index 8 * grp + j <-> key 4 * grp + j of entry
+    // e0 (j < 4) or of entry e0 + 1 (j >= 4).
+    const u32x4 pa = {pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3]),
+                      pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, pa);
+
+    // P.V: lane (col, grp) reads, for each 8-column group cg of its columns, the 8 keys of its
+    // reduction slots (key rows 4 * grp + j and 16 + 4 * grp + j, j < 4) and transposes them
+    // into 8 B operands (one per column).
+    constexpr int kV = SHARED ? 0 : 1;
+#pragma unroll
+    for (int cg = 0; cg < Sh::kVGroups; ++cg) {
+      const int chunk = swz<D>(col * Sh::kVGroups + cg);
+      u32x4 vr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int key = (j < 4 ? 0 : kTile) + 4 * grp + (j & 3);
+        vr[j] = *reinterpret_cast<const u32x4*>(&kv_lds[buf][kV][key][8 * chunk]);
+      }
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const u32x4 be = {__builtin_amdgcn_perm(vr[1][d], vr[0][d], 0x05040100u),
+                          __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x05040100u),
+                          __builtin_amdgcn_perm(vr[5][d], vr[4][d], 0x05040100u),
+                          __builtin_amdgcn_perm(vr[7][d], vr[6][d], 0x05040100u)};
+        const u32x4 bo = {__builtin_amdgcn_perm(vr[1][d], vr[0][d], 0x07060302u),
+                          __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x07060302u),
+                          __builtin_amdgcn_perm(vr[5][d], vr[4][d], 0x07060302u),
+                          __builtin_amdgcn_perm(vr[7][d], vr[6][d], 0x07060302u)};
+        const int e = 8 * cg + 2 * d;
+        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, __builtin_bit_cast(bf16x8, be),
+                                                         acc[e], 0, 0, 0);
+        acc[e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            pop, __builtin_bit_cast(bf16x8, bo), acc[e + 1], 0, 0, 0);
+      }
+    }
+
+    // The next step's tile (already in registers) into the other buffer, then the fetch of the
+    // step after it; one barrier publishes the buffer and retires this step's reads.
+    // (After the last step this stages clamped re-reads of the last entry, which are never used.)
+    full_cur = store_tile(buf ^ 1, e0 + 2, ok_next);
+    ok_cur[0] = ok_next[0];
+    ok_cur[1] = ok_next[1];
+    issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
+                __builtin_amdgcn_readlane(pid_next, 1), ok_next);
+    pid_next = pid_vector(e0 + 6);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // Normalise and write: lane (col, grp) holds rows 16 * wave + 4 * grp + i, columns
+  // col * kLaneCols .. + kLaneCols.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * wave + 4 * grp + i;
+    const float lh = __shfl(l_run, 4 * grp + i);
+    const float inv = lh > 0.f ? 1.f / lh : 0.f;
+    if (row_valid(r)) {
+      float* dst = a.o_part + (out_row(r) * ns + split) * D + col * Sh::kLaneCols;
+#pragma unroll
+      for (int e = 0; e < Sh::kLaneCols; e += 4) {
+        const f32x4 v4 = {acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv,
+                          acc[e + 3][i] * inv};
+        *reinterpret_cast<f32x4*>(dst + e) = v4;
+      }
+    }
+  }
+  if (grp == 0 && row_valid(my_row)) {
+    const float lse = (m_run == -INFINITY) ? -INFINITY : (m_run + __log2f(l_run)) * kLn2;
+    a.lse_part[out_row(my_row) * ns + split] = lse;
+  }
+}
+
+template <int D, int G>
+hipError_t launch(const Stage1Args& args, bool shared, int batch, hipStream_t stream) {
+  dim3 grid(args.num_splits * args.num_qblocks, args.num_kv_heads, batch);
+  void* kargs[] = {const_cast<Stage1Args*>(&args)};
+  const void* fn = shared ? reinterpret_cast<const void*>(&prefill_kernel<D, G, true>)
+                          : reinterpret_cast<const void*>(&prefill_kernel<D, G, false>);
+  return hipLaunchKernel(fn, grid, dim3(kThreads), kargs, 0, stream);
+}
+
+template <int D>
+hipError_t launch_d(const Stage1Args& args, int group_size, bool shared, int batch,
+                    hipStream_t stream) {
+  switch (group_size) {
+    case 1: return launch<D, 1>(args, shared, batch, stream);
+    case 2: return launch<D, 2>(args, shared, batch, stream);
+    case 4: return launch<D, 4>(args, shared, batch, stream);
+    case 8: return launch<D, 8>(args, shared, batch, stream);
+    case 16: return launch<D, 16>(args, shared, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const Stage1Args& args, int head_dim, int group_size, int batch,
+                          hipStream_t stream) {
+  const bool shared = args.k_pool == args.v_pool;
+  switch (head_dim) {
+    case 256: return launch_d<256>(args, group_size, shared, batch, stream);
+    case 512: return launch_d<512>(args, group_size, shared, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace decode_attn
