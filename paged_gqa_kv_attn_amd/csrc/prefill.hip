@@ -36,19 +36,15 @@
 
 #include <hip/hip_runtime.h>
 
+#include "device_common.h"
 #include "internal.h"
 
 namespace decode_attn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStepKeys = 2 * kTile;  // two tile-list entries per loop step
-constexpr float kLn2 = 0.693147180559945309417f;
 
 template <int D>
 struct PShape {
@@ -69,38 +65,6 @@ struct PShape {
 template <int D>
 __device__ __forceinline__ int swz(int c) {
   return c ^ ((c >> 4) & PShape<D>::kSwz);
-}
-
-typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
-__device__ __forceinline__ int32_t load_uniform(const int32_t* p, size_t idx) {
-  return ((const_i32_ptr)(p))[idx];
-}
-
-__device__ __forceinline__ float max_xor16_32(float v) {
-  const uint32_t b = __builtin_bit_cast(uint32_t, v);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  const float m16 = fmaxf(__builtin_bit_cast(float, (uint32_t)r16[0]),
-                          __builtin_bit_cast(float, (uint32_t)r16[1]));
-  const uint32_t c = __builtin_bit_cast(uint32_t, m16);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
-  return fmaxf(__builtin_bit_cast(float, (uint32_t)r32[0]),
-               __builtin_bit_cast(float, (uint32_t)r32[1]));
-}
-
-__device__ __forceinline__ float sum_xor16_32(float v) {
-  const uint32_t b = __builtin_bit_cast(uint32_t, v);
-  const auto r16 = __builtin_amdgcn_permlane16_swap(b, b, false, false);
-  const float s16 = __builtin_bit_cast(float, (uint32_t)r16[0]) +
-                    __builtin_bit_cast(float, (uint32_t)r16[1]);
-  const uint32_t c = __builtin_bit_cast(uint32_t, s16);
-  const auto r32 = __builtin_amdgcn_permlane32_swap(c, c, false, false);
-  return __builtin_bit_cast(float, (uint32_t)r32[0]) + __builtin_bit_cast(float, (uint32_t)r32[1]);
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;  // round to nearest even
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
-         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
 // SHARED: the pools are one buffer (values are the keys); the V tile is the K tile.
