@@ -106,3 +106,28 @@ def test_prefill_workload_global_chunk():
     out, lse = gu.run(inp)
     err, cos = gu.compare(out, lse, *gu.reference(inp), "long_ctx global L256")
     print("  max_abs_err %.3g  min_cos %.7f" % (err, cos), flush=True)
+
+
+@pytest.mark.parametrize("S", [32, 256])
+@pytest.mark.parametrize("D,G,window,sink", [(512, 8, 0, 0), (256, 2, 200, 8)])
+def test_prefill_pages_empty_and_short_sequences(S, D, G, window, sink):
+    """Pages of 32 and 256 keys (tiles are 16-key slices of a page), an empty sequence (all its
+    queries attend nothing: out = 0, lse = -inf), sequences shorter than the chunk, and a
+    window with sinks."""
+    print("prefill pages S=%d D=%d G=%d W=%d sink=%d" % (S, D, G, window, sink), flush=True)
+    Hkv = 2
+    inp = make_layer_inputs([0, 5, 300, 1200], G * Hkv, Hkv, D, page_size=S, window=window,
+                            sink=sink, seed=[77, S, D, window], q_mult=1.5, q_len=100)
+    for splits in (0, 3):
+        out, lse = gu.run(inp, force_splits=splits)
+        gu.compare(out, lse, *gu.reference(inp), "prefill S%d D%d ns%d" % (S, D, splits))
+
+
+def test_prefill_sliding_values_equal_keys():
+    inp = make_layer_inputs([900, 64], 16, 8, 256, page_size=16, window=300, sink=4, seed=78,
+                            q_len=200)
+    inp.v_pool = inp.k_pool
+    t = gu.upload(inp)
+    t["v"] = t["k"]
+    out, lse = gu.run(inp, dev_bufs=t, values_are_keys=True)
+    gu.compare(out, lse, *gu.reference(inp), "prefill sliding k=v")
