@@ -97,7 +97,7 @@ typedef enum {
 /* The shape a plan covers. Values are upper bounds for the calls made with the plan. */
 typedef struct {
   int32_t batch;             /* B >= 1: most sequences per call; B * max(1, q_len) <= 65535 */
-  int32_t num_q_heads;       /* Hq >= 1 */
+  int32_t num_q_heads;       /* 1 <= Hq <= 65535 */
   int32_t num_kv_heads;      /* Hkv >= 1, Hq % Hkv == 0; G = Hq / Hkv in {1, 2, 4, 8, 16} */
   int32_t head_dim;          /* D in {256, 512} */
   int32_t page_size;         /* S: tokens per page, a multiple of 16, 16 <= S <= 1024 */

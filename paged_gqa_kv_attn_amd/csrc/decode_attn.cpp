@@ -204,8 +204,9 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   if (p.max_splits > DECODE_ATTN_MAX_SPLITS_LIMIT || p.force_splits > DECODE_ATTN_MAX_SPLITS_LIMIT)
     return DECODE_ATTN_ERR_SHAPE;
   if ((int64_t)p.max_pages_per_seq * p.page_size > INT32_MAX) return DECODE_ATTN_ERR_SHAPE;
-  // Launch grids put (sequence, query token) pairs on a grid dimension capped at 65535.
+  // Launch grids put (sequence, query token) pairs, and heads, on grid dimensions capped at 65535.
   if ((int64_t)p.batch * (p.q_len > 1 ? p.q_len : 1) > 65535) return DECODE_ATTN_ERR_SHAPE;
+  if (p.num_q_heads > 65535) return DECODE_ATTN_ERR_SHAPE;
   const int G = p.num_q_heads / p.num_kv_heads;
   if (p.page_size % kTile != 0 || p.page_size > 1024) return DECODE_ATTN_ERR_UNSUPPORTED;
   if (!stage1_supported(p.head_dim, G)) return DECODE_ATTN_ERR_UNSUPPORTED;

@@ -139,6 +139,7 @@ def test_plan_force_and_cap():
     (dict(window=64, sink=-1), ERR_SHAPE),
     (dict(q_len=-1), ERR_SHAPE),
     (dict(q_len=8193), ERR_SHAPE),
+    (dict(num_q_heads=65536 * 2, num_kv_heads=2), ERR_SHAPE),  # heads past a grid dimension
     (dict(batch=4096, q_len=16), ERR_SHAPE),     # 65536 (sequence, token) pairs
     (dict(force_splits=1025), ERR_SHAPE),
     (dict(max_splits=2000), ERR_SHAPE),
