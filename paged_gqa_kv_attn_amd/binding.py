@@ -132,8 +132,9 @@ def _check(status: int, where: str) -> None:
         raise DecodeAttnError(status, where)
 
 
-def _dev_ptr(x, name: str, dtype=None) -> Optional[int]:
-    """Device address of a torch CUDA tensor (checked) or a raw integer address; None -> NULL."""
+def _dev_ptr(x, name: str, dtype=None, device: Optional[int] = None) -> Optional[int]:
+    """Device address of a torch CUDA tensor (checked, on ``device`` when given) or a raw integer
+    address; None -> NULL."""
     if x is None:
         return None
     if isinstance(x, int):
@@ -143,6 +144,9 @@ def _dev_ptr(x, name: str, dtype=None) -> Optional[int]:
         raise TypeError("%s must be a torch CUDA tensor or an integer device address" % name)
     if not x.is_cuda:
         raise ValueError("%s must live in device memory" % name)
+    if device is not None and x.get_device() != device:
+        raise ValueError("%s lives on cuda:%d; the call launches on the current device cuda:%d"
+                         % (name, x.get_device(), device))
     if not x.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and x.dtype != dtype:
@@ -176,6 +180,11 @@ def _check_sizes(plan, batch, q=None, k_pool=None, v_pool=None, block_table=None
     _need(ctx_lens, "ctx_lens", int(batch))
     _need(out, "out", rows * p.head_dim)
     _need(lse_out, "lse_out", rows)
+
+
+def _current_device() -> Optional[int]:
+    import torch
+    return torch.cuda.current_device() if torch.cuda.is_available() else None
 
 
 def _stream_handle(stream) -> Optional[int]:
@@ -218,22 +227,25 @@ def _f32():
     return torch.float32
 
 
-def _ws(workspace, workspace_bytes):
+def _ws(workspace, workspace_bytes, device=None):
     if workspace_bytes is None:
-        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else _nbytes(workspace)
-    return _dev_ptr(workspace, "workspace"), int(workspace_bytes)
+        raw = workspace is None or isinstance(workspace, int)
+        workspace_bytes = 0 if raw else _nbytes(workspace)
+    return _dev_ptr(workspace, "workspace", None, device), int(workspace_bytes)
 
 
 def decode_attn_global(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, out,
                        lse_out=None, workspace=None, workspace_bytes=None, stream=None) -> None:
     lib = load_library()
+    dev = _current_device()
     _check_sizes(plan, batch, q, k_pool, v_pool, block_table, ctx_lens, out, lse_out)
-    ws, wsb = _ws(workspace, workspace_bytes)
+    ws, wsb = _ws(workspace, workspace_bytes, dev)
     _check(lib.decode_attn_global(
-        ctypes.byref(plan), _dev_ptr(q, "q", _bf16()), _dev_ptr(k_pool, "k_pool", _bf16()),
-        _dev_ptr(v_pool, "v_pool", _bf16()), _dev_ptr(block_table, "block_table", _i32()),
-        _dev_ptr(ctx_lens, "ctx_lens", _i32()), int(batch), float(scale),
-        _dev_ptr(out, "out", _f32()), _dev_ptr(lse_out, "lse_out", _f32()), ws, wsb,
+        ctypes.byref(plan), _dev_ptr(q, "q", _bf16(), dev),
+        _dev_ptr(k_pool, "k_pool", _bf16(), dev), _dev_ptr(v_pool, "v_pool", _bf16(), dev),
+        _dev_ptr(block_table, "block_table", _i32(), dev),
+        _dev_ptr(ctx_lens, "ctx_lens", _i32(), dev), int(batch), float(scale),
+        _dev_ptr(out, "out", _f32(), dev), _dev_ptr(lse_out, "lse_out", _f32(), dev), ws, wsb,
         _stream_handle(stream)), "decode_attn_global")
 
 
@@ -241,36 +253,41 @@ def decode_attn_sliding(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, ba
                         out, lse_out=None, workspace=None, workspace_bytes=None,
                         stream=None) -> None:
     lib = load_library()
+    dev = _current_device()
     _check_sizes(plan, batch, q, k_pool, v_pool, block_table, ctx_lens, out, lse_out)
-    ws, wsb = _ws(workspace, workspace_bytes)
+    ws, wsb = _ws(workspace, workspace_bytes, dev)
     _check(lib.decode_attn_sliding(
-        ctypes.byref(plan), _dev_ptr(q, "q", _bf16()), _dev_ptr(k_pool, "k_pool", _bf16()),
-        _dev_ptr(v_pool, "v_pool", _bf16()), _dev_ptr(block_table, "block_table", _i32()),
-        _dev_ptr(ctx_lens, "ctx_lens", _i32()), int(batch), int(window), float(scale),
-        _dev_ptr(out, "out", _f32()), _dev_ptr(lse_out, "lse_out", _f32()), ws, wsb,
+        ctypes.byref(plan), _dev_ptr(q, "q", _bf16(), dev),
+        _dev_ptr(k_pool, "k_pool", _bf16(), dev), _dev_ptr(v_pool, "v_pool", _bf16(), dev),
+        _dev_ptr(block_table, "block_table", _i32(), dev),
+        _dev_ptr(ctx_lens, "ctx_lens", _i32(), dev), int(batch), int(window), float(scale),
+        _dev_ptr(out, "out", _f32(), dev), _dev_ptr(lse_out, "lse_out", _f32(), dev), ws, wsb,
         _stream_handle(stream)), "decode_attn_sliding")
 
 
 def decode_attn_stage1(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale,
                        workspace, workspace_bytes=None, stream=None) -> None:
     lib = load_library()
+    dev = _current_device()
     _check_sizes(plan, batch, q, k_pool, v_pool, block_table, ctx_lens)
-    ws, wsb = _ws(workspace, workspace_bytes)
+    ws, wsb = _ws(workspace, workspace_bytes, dev)
     _check(lib.decode_attn_stage1(
-        ctypes.byref(plan), _dev_ptr(q, "q", _bf16()), _dev_ptr(k_pool, "k_pool", _bf16()),
-        _dev_ptr(v_pool, "v_pool", _bf16()), _dev_ptr(block_table, "block_table", _i32()),
-        _dev_ptr(ctx_lens, "ctx_lens", _i32()), int(batch), float(scale), ws, wsb,
+        ctypes.byref(plan), _dev_ptr(q, "q", _bf16(), dev),
+        _dev_ptr(k_pool, "k_pool", _bf16(), dev), _dev_ptr(v_pool, "v_pool", _bf16(), dev),
+        _dev_ptr(block_table, "block_table", _i32(), dev),
+        _dev_ptr(ctx_lens, "ctx_lens", _i32(), dev), int(batch), float(scale), ws, wsb,
         _stream_handle(stream)), "decode_attn_stage1")
 
 
 def decode_attn_stage2(plan: Plan, batch, workspace, out, lse_out=None, workspace_bytes=None,
                        stream=None) -> None:
     lib = load_library()
+    dev = _current_device()
     _check_sizes(plan, batch, out=out, lse_out=lse_out)
-    ws, wsb = _ws(workspace, workspace_bytes)
+    ws, wsb = _ws(workspace, workspace_bytes, dev)
     _check(lib.decode_attn_stage2(
-        ctypes.byref(plan), int(batch), ws, wsb, _dev_ptr(out, "out", _f32()),
-        _dev_ptr(lse_out, "lse_out", _f32()), _stream_handle(stream)), "decode_attn_stage2")
+        ctypes.byref(plan), int(batch), ws, wsb, _dev_ptr(out, "out", _f32(), dev),
+        _dev_ptr(lse_out, "lse_out", _f32(), dev), _stream_handle(stream)), "decode_attn_stage2")
 
 
 def decode_attn_append_kv(plan: Plan, k_new, v_new, k_pool, v_pool, block_table, ctx_lens, batch,
@@ -278,6 +295,7 @@ def decode_attn_append_kv(plan: Plan, k_new, v_new, k_pool, v_pool, block_table,
     """Write each sequence's L = plan q_len newest K/V (positions ctx_lens[b] - L ..) into the
     pools. Passing the same tensor as k_pool and v_pool writes K only (v_new may be None)."""
     lib = load_library()
+    dev = _current_device()
     p = plan.problem
     new = int(batch) * max(1, p.q_len) * p.num_kv_heads * p.head_dim
     _need(k_new, "k_new", new)
@@ -286,9 +304,11 @@ def decode_attn_append_kv(plan: Plan, k_new, v_new, k_pool, v_pool, block_table,
     _check_sizes(plan, batch, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
                  ctx_lens=ctx_lens)
     _check(lib.decode_attn_append_kv(
-        ctypes.byref(plan), _dev_ptr(k_new, "k_new", _bf16()), _dev_ptr(v_new, "v_new", _bf16()),
-        _dev_ptr(k_pool, "k_pool", _bf16()), _dev_ptr(v_pool, "v_pool", _bf16()),
-        _dev_ptr(block_table, "block_table", _i32()), _dev_ptr(ctx_lens, "ctx_lens", _i32()),
+        ctypes.byref(plan), _dev_ptr(k_new, "k_new", _bf16(), dev),
+        _dev_ptr(v_new, "v_new", _bf16(), dev),
+        _dev_ptr(k_pool, "k_pool", _bf16(), dev), _dev_ptr(v_pool, "v_pool", _bf16(), dev),
+        _dev_ptr(block_table, "block_table", _i32(), dev),
+        _dev_ptr(ctx_lens, "ctx_lens", _i32(), dev),
         int(batch), _stream_handle(stream)), "decode_attn_append_kv")
 
 
