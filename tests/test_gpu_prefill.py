@@ -108,17 +108,17 @@ def test_prefill_workload_global_chunk():
     print("  max_abs_err %.3g  min_cos %.7f" % (err, cos), flush=True)
 
 
-@pytest.mark.parametrize("S", [32, 256])
+@pytest.mark.parametrize("S", [32, 256, 1024])
 @pytest.mark.parametrize("D,G,window,sink", [(512, 8, 0, 0), (256, 2, 200, 8)])
 def test_prefill_pages_empty_and_short_sequences(S, D, G, window, sink):
-    """Pages of 32 and 256 keys (tiles are 16-key slices of a page), an empty sequence (all its
-    queries attend nothing: out = 0, lse = -inf), sequences shorter than the chunk, and a
-    window with sinks."""
+    """Pages of 32 to 1024 keys (tiles are 16-key slices of a page), an empty sequence (all its
+    queries attend nothing: out = 0, lse = -inf), sequences shorter than the chunk, a window with
+    sinks, and 64 forced splits (most of them empty for the short sequences)."""
     print("prefill pages S=%d D=%d G=%d W=%d sink=%d" % (S, D, G, window, sink), flush=True)
     Hkv = 2
     inp = make_layer_inputs([0, 5, 300, 1200], G * Hkv, Hkv, D, page_size=S, window=window,
                             sink=sink, seed=[77, S, D, window], q_mult=1.5, q_len=100)
-    for splits in (0, 3):
+    for splits in (0, 3, 64):
         out, lse = gu.run(inp, force_splits=splits)
         gu.compare(out, lse, *gu.reference(inp), "prefill S%d D%d ns%d" % (S, D, splits))
 
