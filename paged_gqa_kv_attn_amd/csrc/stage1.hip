@@ -120,7 +120,11 @@ struct StepRegs {
 // GENERAL: several query tokens per sequence and/or sink keys. Without it (one query token, no
 // sinks) the row bounds are uniform and the query-block and sink arithmetic folds away.
 // RG: groups of 16 MFMA rows per workgroup (2 only with GENERAL): 16 * RG rows share every tile
-// read, so up to 32 / G query tokens cost one pass over the keys.
+// read, so up to 32 / G query tokens cost one pass over the keys (a sequence with 64 rows or more
+// per kv head runs on the prefill kernel instead, prefill.hip).
+// STREAM: no other workgroup reads this block's tiles (one query block per sequence), so K/V
+// loads carry the non-temporal hint; with several query blocks they are ordinary loads and the
+// L2 serves the blocks' re-reads.
 template <int D, int G, int SUB, bool SHARED, bool GENERAL, int RG, bool STREAM>
 __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const Stage1Args a) {
   using Sh = Shape<D, RG>;
