@@ -176,3 +176,41 @@ def test_many_sequences():
     inp = make_layer_inputs(ctx, 16, 8, 256, page_size=16, window=512, seed=34)
     out, lse = gu.run(inp)
     gu.compare(out, lse, *gu.reference(inp), "batch 96")
+
+
+@pytest.mark.parametrize("D,G,window,L", [(512, 8, 0, 1), (512, 8, 0, 128), (256, 2, 300, 1),
+                                          (256, 2, 300, 96)])
+def test_pools_beyond_4gib(D, G, window, L):
+    """Pools of 4.6 GB whose used pages sit past the first 4 GiB: every K/V address is a 64-bit
+    offset. The attended pages of a compact layer are copied to high page ids of a large pool
+    (the rest of the pool is left uninitialised and never read) and the result must equal the
+    oracle on the compact layer, for decode and for a prefill chunk."""
+    import torch
+    print("big pools D=%d G=%d W=%d L=%d" % (D, G, window, L), flush=True)
+    Hkv = 2
+    inp = make_layer_inputs([1000, 777], G * Hkv, Hkv, D, page_size=16, window=window,
+                            seed=[81, D, L], q_len=L)
+    ref = gu.reference(inp)
+    d = inp.dims
+    page_bytes = Hkv * 16 * D * 2
+    big = (9 << 29) // page_bytes              # ~4.8 GB per pool
+    first_high = (4 << 30) // page_bytes + 1   # page ids from here start past 4 GiB
+    rng = np.random.default_rng(82)
+    high = rng.choice(np.arange(first_high, big), size=d["P"], replace=False)
+    table = inp.block_table.copy()
+    valid = (table >= 0) & (table < d["P"])
+    table[valid] = high[table[valid]]
+    dev = gu.device()
+    t = gu.upload(inp)
+    idx = torch.from_numpy(high).to(dev)
+    kb = torch.empty((big, Hkv, 16, D), dtype=torch.bfloat16, device=dev)
+    vb = torch.empty((big, Hkv, 16, D), dtype=torch.bfloat16, device=dev)
+    kb[idx] = t["k"]
+    vb[idx] = t["v"]
+    t["k"], t["v"] = kb, vb
+    t["bt"] = torch.from_numpy(table).to(dev)
+    plan = gu.make_plan(inp, num_pages=big)
+    out, lse = gu.run(inp, plan=plan, dev_bufs=t)
+    gu.compare(out, lse, *ref, "big pools D%d L%d" % (D, L))
+    del kb, vb, t
+    torch.cuda.empty_cache()
