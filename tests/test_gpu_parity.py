@@ -214,3 +214,36 @@ def test_pools_beyond_4gib(D, G, window, L):
     gu.compare(out, lse, *ref, "big pools D%d L%d" % (D, L))
     del kb, vb, t
     torch.cuda.empty_cache()
+
+
+def test_append_beyond_4gib():
+    """The paged append into a 4.8 GB pool whose target pages lie past the first 4 GiB: the new
+    tokens land in their slots, bit for bit."""
+    import torch
+    import paged_gqa_kv_attn_amd as pda
+    gu.ensure_library()
+    D, Hkv, S, L = 512, 2, 16, 3
+    ctx = np.array([1000, 77], dtype=np.int32)
+    page_bytes = Hkv * S * D * 2
+    big = (9 << 29) // page_bytes
+    first_high = (4 << 30) // page_bytes + 1
+    M = 64
+    rng = np.random.default_rng(83)
+    table = rng.choice(np.arange(first_high, big), size=(2, M), replace=False).astype(np.int32)
+    dev = gu.device()
+    kb = torch.zeros((big, Hkv, S, D), dtype=torch.bfloat16, device=dev)
+    vb = torch.zeros((big, Hkv, S, D), dtype=torch.bfloat16, device=dev)
+    k_new = torch.randn((2, L, Hkv, D), device=dev).to(torch.bfloat16)
+    v_new = torch.randn((2, L, Hkv, D), device=dev).to(torch.bfloat16)
+    plan = pda.decode_attn_plan(2, 8 * Hkv, Hkv, D, S, M, big, max_ctx_len=1000, q_len=L)
+    pda.decode_attn_append_kv(plan, k_new, v_new, kb, vb, torch.from_numpy(table).to(dev),
+                              torch.from_numpy(ctx).to(dev), 2)
+    torch.cuda.synchronize()
+    for b in range(2):
+        for i in range(L):
+            tpos = int(ctx[b]) - L + i
+            page = int(table[b, tpos // S])
+            assert torch.equal(kb[page, :, tpos % S], k_new[b, i])
+            assert torch.equal(vb[page, :, tpos % S], v_new[b, i])
+    del kb, vb
+    torch.cuda.empty_cache()
