@@ -274,8 +274,8 @@ def main() -> int:
 
     detail = {}
     for L in layers:
-        us = timed_calls(L, 20, flush=True)
-        hot = timed_calls(L, 20, flush=False)
+        us = timed_calls(L, 50, flush=True)
+        hot = timed_calls(L, 50, flush=False)
         med = us[len(us) // 2]
         if args.append:
             eva = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -322,6 +322,9 @@ def main() -> int:
         "unit": "GB/s",
         "frac": round(achieved / PEAK_HBM_GBS, 4),
         "traffic": traffic,
+        "traffic_GB_per_s": (round(traffic / (s1_avg_us * 1e-6) / 1e9, 1)
+                             if traffic is not None else None),
+        "traffic_over_algorithmic": round(traffic / s1_bytes, 4) if traffic is not None else None,
         "avg_launch_us": round(s1_avg_us, 3),
         "algorithmic_bytes_per_launch": s1_bytes,
         "algorithmic_flops_per_launch": s1_flops,
