@@ -219,13 +219,73 @@ int decode_attn_append_kv(const decode_attn_plan_t* plan, const void* k_new, con
                           void* k_pool, void* v_pool, const int32_t* block_table,
                           const int32_t* ctx_lens, int32_t batch, void* stream);
 
+/* Normalisation flags of decode_attn_append_kv_rope. */
+#define DECODE_ATTN_NORM_QK 1 /* RMSNorm every q head and every new k head before the rotation */
+#define DECODE_ATTN_NORM_V 2  /* RMSNorm every new v head (values are never rotated) */
+
+/*
+ * decode_attn_rope_cache — fill the rotation table that decode_attn_append_kv_rope reads, for one
+ * layer configuration (Sparse-vLLM PR #27, section "Gemma 4 文本推理": each layer kind has its own
+ * RoPE parameters and its own RoPE cache). With R = rotary_dim, for t < max_position and j < R/2:
+ *     f_j = theta^(-2j / F)            F = freq_dim, or R when freq_dim = 0
+ *     cos_sin[t, j] = cos(t * f_j),    cos_sin[t, R/2 + j] = sin(t * f_j)
+ * computed on the device in double precision and rounded to fp32. cos_sin: [max_position, R] fp32
+ * device memory owned by the caller, 4-byte aligned. A table of any other RoPE variant (scaled
+ * positions or frequencies) has the same layout and can be written by the caller instead.
+ * Errors: ERR_NULL (cos_sin NULL), ERR_ALIGN, ERR_SHAPE (max_position < 1, R odd or < 2,
+ * freq_dim < 0, theta not finite and positive). Asynchronous on `stream`.
+ */
+int decode_attn_rope_cache(float* cos_sin, int32_t max_position, int32_t rotary_dim,
+                           int32_t freq_dim, double theta, void* stream);
+
+/*
+ * decode_attn_append_kv_rope — the step just before attention as one launch: QK-norm, rotary
+ * position embedding and the paged append (Sparse-vLLM PR #27, section "专用算子与性能优化": a
+ * dedicated QKV-norm + RoPE operator; vLLM learning notes "模型库与算子层 — 概念", section
+ * "自定义 Inductor 融合 pass": norm/RoPE fused with the paged KV-cache write, and section
+ * "内核框架（Helion）": the q/k RMSNorm fused with RoPE in place, NeoX or GPT-J pairing).
+ * For b < batch, new token i < L = plan->problem.q_len and its position t = ctx_lens[b] - L + i:
+ *     rms(x; w)  = x / sqrt(mean_d x_d^2 + eps) * w       (w NULL: no scale)
+ *     q_out[b, i, h]           = rope_t(rms(q[b, i, h]; q_norm_weight))
+ *     k_pool[page, g, t % S]   = rope_t(rms(k_new[b, i, g]; k_norm_weight))
+ *     v_pool[page, g, t % S]   = rms(v_new[b, i, g]; v_norm_weight)
+ * with page = block_table[b, t / S]; rms is applied to q and k only with DECODE_ATTN_NORM_QK and
+ * to v only with DECODE_ATTN_NORM_V (else v is copied bit for bit). rope_t turns pair j < R/2 of
+ * the first R = rotary_dim dims, (x1, x2) -> (x1 c - x2 s, x2 c + x1 s) with c = cos_sin[t, j] and
+ * s = cos_sin[t, R/2 + j]; the pair is (x_j, x_{j+R/2}) for interleaved = 0 (NeoX) and
+ * (x_{2j}, x_{2j+1}) for interleaved = 1 (GPT-J); dims at or past R pass unchanged (R = 0: no
+ * rotation, cos_sin may be NULL). Arithmetic is fp32; every output is rounded once to bf16.
+ *
+ * Arguments: q and q_out [B, L, Hq, D] bf16 ([B, Hq, D] when L = 1), q_out == q for in place, else
+ * not overlapping; k_new, v_new [B, L, Hkv, D] bf16; pools, block_table and ctx_lens as for
+ * attention; v_pool == k_pool for layers whose values are their keys (then only k is written and
+ * v_new may be NULL); cos_sin [max_position, R] fp32 (decode_attn_rope_cache); the norm weights [D]
+ * fp32 or NULL. bf16 buffers 16-byte aligned, the others 4-byte. Any plan of the layer with the
+ * same q_len can be used (only its shape is read). Asynchronous on `stream`.
+ *
+ * Skips: a token with t < 0 or t >= max_position is skipped whole (its q_out row is not written,
+ * nothing is appended). A page column t / S past the table row or a page id outside [0, P) skips
+ * that token's k and v writes (its q_out row is still written).
+ * Errors: ERR_PLAN, ERR_SHAPE (batch outside [0, plan batch], R odd or outside [0, D],
+ * max_position < 1, interleaved not 0 or 1, unknown flags, eps not finite and positive while a
+ * norm flag is set), ERR_NULL, ERR_ALIGN, ERR_HIP.
+ */
+int decode_attn_append_kv_rope(const decode_attn_plan_t* plan, const void* q, void* q_out,
+                               const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                               const int32_t* block_table, const int32_t* ctx_lens, int32_t batch,
+                               const float* cos_sin, int32_t max_position, int32_t rotary_dim,
+                               int32_t interleaved, int32_t norm_flags, const float* q_norm_weight,
+                               const float* k_norm_weight, const float* v_norm_weight, float eps,
+                               void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_str(int status);
 
 /* Library version, major * 10000 + minor * 100 + patch. The minor number changes with the layout
  * of decode_attn_problem / decode_attn_plan_t (0.2: sink and q_len fields); 0.2.1: q_len up to
- * 8192, one-split calls without stage 2. */
-#define DECODE_ATTN_VERSION 201
+ * 8192, one-split calls without stage 2; 0.2.2: decode_attn_rope_cache and
+ * decode_attn_append_kv_rope. */
+#define DECODE_ATTN_VERSION 202
 int decode_attn_version(void);
 
 #ifdef __cplusplus

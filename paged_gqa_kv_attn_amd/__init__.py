@@ -6,11 +6,15 @@ PyTorch only supplies device memory and the current stream. The library is loade
 and a missing or unloadable library raises an error: there is no fallback.
 """
 from .binding import (  # noqa: F401
+    NORM_QK,
+    NORM_V,
     DecodeAttnError,
     Plan,
     decode_attn_append_kv,
+    decode_attn_append_kv_rope,
     decode_attn_global,
     decode_attn_plan,
+    decode_attn_rope_cache,
     decode_attn_sliding,
     decode_attn_stage1,
     decode_attn_stage2,

@@ -74,7 +74,7 @@ def library_path() -> str:
 
 
 # decode_attn_version() of the library whose struct layouts Problem and Plan mirror.
-ABI_VERSION = 201
+ABI_VERSION = 202
 
 
 def load_library():
@@ -101,8 +101,12 @@ def load_library():
     lib.decode_attn_stage1.argtypes = [pplan, vp, vp, vp, vp, vp, i32, f32, vp, u64, vp]
     lib.decode_attn_stage2.argtypes = [pplan, i32, vp, u64, vp, vp, vp]
     lib.decode_attn_append_kv.argtypes = [pplan, vp, vp, vp, vp, vp, vp, i32, vp]
+    lib.decode_attn_rope_cache.argtypes = [vp, i32, i32, i32, ctypes.c_double, vp]
+    lib.decode_attn_append_kv_rope.argtypes = [pplan, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
+                                               i32, i32, i32, vp, vp, vp, f32, vp]
     for fn in ("decode_attn_plan", "decode_attn_global", "decode_attn_sliding",
-               "decode_attn_stage1", "decode_attn_stage2", "decode_attn_append_kv"):
+               "decode_attn_stage1", "decode_attn_stage2", "decode_attn_append_kv",
+               "decode_attn_rope_cache", "decode_attn_append_kv_rope"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.decode_attn_status_str.argtypes = [ctypes.c_int]
     lib.decode_attn_status_str.restype = ctypes.c_char_p
@@ -310,6 +314,60 @@ def decode_attn_append_kv(plan: Plan, k_new, v_new, k_pool, v_pool, block_table,
         _dev_ptr(block_table, "block_table", _i32(), dev),
         _dev_ptr(ctx_lens, "ctx_lens", _i32(), dev),
         int(batch), _stream_handle(stream)), "decode_attn_append_kv")
+
+
+NORM_QK = 1  # RMSNorm q and the new k heads before the rotation
+NORM_V = 2   # RMSNorm the new v heads
+
+
+def decode_attn_rope_cache(cos_sin, max_position, rotary_dim, theta, freq_dim=0,
+                           stream=None) -> None:
+    """Fill cos_sin [max_position, rotary_dim] fp32 with cos(t f_j) then sin(t f_j), f_j =
+    theta^(-2j / (freq_dim or rotary_dim)), computed on the device in double precision."""
+    lib = load_library()
+    dev = _current_device()
+    _need(cos_sin, "cos_sin", int(max_position) * int(rotary_dim))
+    _check(lib.decode_attn_rope_cache(_dev_ptr(cos_sin, "cos_sin", _f32(), dev), int(max_position),
+                                      int(rotary_dim), int(freq_dim), float(theta),
+                                      _stream_handle(stream)), "decode_attn_rope_cache")
+
+
+def decode_attn_append_kv_rope(plan: Plan, q, q_out, k_new, v_new, k_pool, v_pool, block_table,
+                               ctx_lens, batch, cos_sin, max_position, rotary_dim,
+                               interleaved=False, norm_flags=0, q_norm_weight=None,
+                               k_norm_weight=None, v_norm_weight=None, eps=1e-6,
+                               stream=None) -> None:
+    """QK-norm + RoPE of the new tokens' q (into q_out, which may be q) and k, and the paged append
+    of k and v (v optionally normalised), in one launch. Passing the same tensor as k_pool and
+    v_pool writes K only (v_new may be None)."""
+    lib = load_library()
+    dev = _current_device()
+    p = plan.problem
+    L = max(1, p.q_len)
+    new = int(batch) * L * p.num_kv_heads * p.head_dim
+    _need(q_out, "q_out", int(batch) * L * p.num_q_heads * p.head_dim)
+    _need(k_new, "k_new", new)
+    if v_pool is not k_pool:
+        _need(v_new, "v_new", new)
+    if int(rotary_dim) > 0:
+        _need(cos_sin, "cos_sin", int(max_position) * int(rotary_dim))
+    for w, name in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight"),
+                    (v_norm_weight, "v_norm_weight")):
+        _need(w, name, p.head_dim)
+    _check_sizes(plan, batch, q=q, k_pool=k_pool, v_pool=v_pool, block_table=block_table,
+                 ctx_lens=ctx_lens)
+    _check(lib.decode_attn_append_kv_rope(
+        ctypes.byref(plan), _dev_ptr(q, "q", _bf16(), dev), _dev_ptr(q_out, "q_out", _bf16(), dev),
+        _dev_ptr(k_new, "k_new", _bf16(), dev), _dev_ptr(v_new, "v_new", _bf16(), dev),
+        _dev_ptr(k_pool, "k_pool", _bf16(), dev), _dev_ptr(v_pool, "v_pool", _bf16(), dev),
+        _dev_ptr(block_table, "block_table", _i32(), dev),
+        _dev_ptr(ctx_lens, "ctx_lens", _i32(), dev), int(batch),
+        _dev_ptr(cos_sin, "cos_sin", _f32(), dev), int(max_position), int(rotary_dim),
+        int(bool(interleaved)), int(norm_flags),
+        _dev_ptr(q_norm_weight, "q_norm_weight", _f32(), dev),
+        _dev_ptr(k_norm_weight, "k_norm_weight", _f32(), dev),
+        _dev_ptr(v_norm_weight, "v_norm_weight", _f32(), dev), float(eps),
+        _stream_handle(stream)), "decode_attn_append_kv_rope")
 
 
 def decode_attn_status_str(status: int) -> str:

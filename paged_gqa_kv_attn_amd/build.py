@@ -16,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdecode_attn.so")
-SOURCES = ["decode_attn.cpp", "stage1.hip", "prefill.hip", "stage2.hip", "append.hip"]
+SOURCES = ["decode_attn.cpp", "stage1.hip", "prefill.hip", "stage2.hip", "append.hip",
+           "append_rope.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU instructions are kept out of the generated code.

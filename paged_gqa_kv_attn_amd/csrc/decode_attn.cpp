@@ -338,6 +338,74 @@ int decode_attn_append_kv(const decode_attn_plan_t* plan, const void* k_new, con
   return DECODE_ATTN_OK;
 }
 
+int decode_attn_rope_cache(float* cos_sin, int32_t max_position, int32_t rotary_dim,
+                           int32_t freq_dim, double theta, void* stream) {
+  if (!cos_sin) return DECODE_ATTN_ERR_NULL;
+  if (!aligned(cos_sin, 4)) return DECODE_ATTN_ERR_ALIGN;
+  if (max_position < 1 || rotary_dim < 2 || rotary_dim % 2 != 0 || freq_dim < 0 ||
+      !(theta > 0.0) || !std::isfinite(theta))
+    return DECODE_ATTN_ERR_SHAPE;
+  if (launch_rope_cache(cos_sin, max_position, rotary_dim, freq_dim ? freq_dim : rotary_dim, theta,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DECODE_ATTN_ERR_HIP;
+  return DECODE_ATTN_OK;
+}
+
+int decode_attn_append_kv_rope(const decode_attn_plan_t* plan, const void* q, void* q_out,
+                               const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                               const int32_t* block_table, const int32_t* ctx_lens, int32_t batch,
+                               const float* cos_sin, int32_t max_position, int32_t rotary_dim,
+                               int32_t interleaved, int32_t norm_flags, const float* q_norm_weight,
+                               const float* k_norm_weight, const float* v_norm_weight, float eps,
+                               void* stream) {
+  const int rc = check_plan(plan);
+  if (rc != DECODE_ATTN_OK) return rc;
+  const decode_attn_problem& p = plan->problem;
+  if (batch < 0 || batch > p.batch) return DECODE_ATTN_ERR_SHAPE;
+  if (rotary_dim < 0 || rotary_dim > p.head_dim || rotary_dim % 2 != 0 || max_position < 1 ||
+      (interleaved != 0 && interleaved != 1) ||
+      (norm_flags & ~(DECODE_ATTN_NORM_QK | DECODE_ATTN_NORM_V)) != 0 ||
+      (norm_flags != 0 && !(eps > 0.f && std::isfinite(eps))))
+    return DECODE_ATTN_ERR_SHAPE;
+  if (batch == 0) return DECODE_ATTN_OK;
+  const bool same = v_pool == k_pool;
+  if (!q || !q_out || !k_new || !k_pool || !v_pool || !block_table || !ctx_lens ||
+      (!same && !v_new) || (rotary_dim > 0 && !cos_sin))
+    return DECODE_ATTN_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(q_out, 16) || !aligned(k_new, 16) || !aligned(k_pool, 16) ||
+      !aligned(v_pool, 16) || (!same && !aligned(v_new, 16)) || !aligned(block_table, 4) ||
+      !aligned(ctx_lens, 4) || !aligned(cos_sin, 4) || !aligned(q_norm_weight, 4) ||
+      !aligned(k_norm_weight, 4) || !aligned(v_norm_weight, 4))
+    return DECODE_ATTN_ERR_ALIGN;
+  AppendRopeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(same ? k_new : v_new);
+  a.k_pool = static_cast<uint16_t*>(k_pool);
+  a.v_pool = static_cast<uint16_t*>(v_pool);
+  a.block_table = block_table;
+  a.ctx_lens = ctx_lens;
+  a.cos_sin = cos_sin;
+  a.q_weight = q_norm_weight;
+  a.k_weight = k_norm_weight;
+  a.v_weight = v_norm_weight;
+  a.eps = eps;
+  a.num_q_heads = p.num_q_heads;
+  a.num_kv_heads = p.num_kv_heads;
+  a.page_size = p.page_size;
+  a.max_pages_per_seq = p.max_pages_per_seq;
+  a.num_pages = p.num_pages;
+  a.q_len = q_len_of(p);
+  a.max_position = max_position;
+  a.rotary_dim = rotary_dim;
+  a.interleaved = interleaved;
+  a.norm_flags = norm_flags;
+  if (launch_append_rope(a, p.head_dim, batch, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return DECODE_ATTN_ERR_HIP;
+  return DECODE_ATTN_OK;
+}
+
 const char* decode_attn_status_str(int status) {
   switch (status) {
     case DECODE_ATTN_OK: return "DECODE_ATTN_OK";

@@ -64,6 +64,33 @@ struct AppendArgs {
   int32_t q_len;                // L >= 1 new tokens per sequence
 };
 
+// Kernel arguments of the fused QK-norm + RoPE + paged append (one wave per (new token, row)).
+struct AppendRopeArgs {
+  const uint16_t* q;            // [B, L, Hq, D] bf16
+  uint16_t* q_out;              // [B, L, Hq, D] bf16, may equal q
+  const uint16_t* k_new;        // [B, L, Hkv, D] bf16
+  const uint16_t* v_new;        // [B, L, Hkv, D] bf16 (unused when v_pool == k_pool)
+  uint16_t* k_pool;             // [P, Hkv, S, D] bf16
+  uint16_t* v_pool;             // [P, Hkv, S, D] bf16, may equal k_pool
+  const int32_t* block_table;   // [B, max_pages_per_seq]
+  const int32_t* ctx_lens;      // [B]
+  const float* cos_sin;         // [max_position, rotary_dim] fp32: cos of pair j, then sin
+  const float* q_weight;        // [D] fp32 or nullptr (unit scale)
+  const float* k_weight;        // [D] fp32 or nullptr
+  const float* v_weight;        // [D] fp32 or nullptr
+  float eps;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+  int32_t q_len;                // L >= 1 new tokens per sequence
+  int32_t max_position;         // positions at or past this are skipped
+  int32_t rotary_dim;           // R, even, 0 = no rotation
+  int32_t interleaved;          // 0: pairs (j, j + R/2); 1: pairs (2j, 2j + 1)
+  int32_t norm_flags;           // bit 0: RMSNorm q and k; bit 1: RMSNorm v
+};
+
 // Launchers (stage1.hip / stage2.hip / append.hip). They return the launch status only. Stage 1
 // picks its single-read variant when k_pool == v_pool.
 hipError_t launch_stage1(const Stage1Args& args, int head_dim, int group_size, int batch,
@@ -73,6 +100,11 @@ hipError_t launch_stage2(const Stage2Args& args, int batch, hipStream_t stream);
 hipError_t launch_prefill(const Stage1Args& args, int head_dim, int group_size, int batch,
                           hipStream_t stream);
 hipError_t launch_append(const AppendArgs& args, int batch, hipStream_t stream);
+// append_rope.hip: the rotation table, then the fused QK-norm + RoPE + append (head_dim 256 or 512).
+hipError_t launch_rope_cache(float* cos_sin, int max_position, int rotary_dim, int freq_dim,
+                             double theta, hipStream_t stream);
+hipError_t launch_append_rope(const AppendRopeArgs& args, int head_dim, int batch,
+                              hipStream_t stream);
 
 // True when a stage-1 kernel is compiled for (head_dim, group_size).
 bool stage1_supported(int head_dim, int group_size);

@@ -235,6 +235,20 @@ def make_layer_inputs(ctx_lens: Sequence[int], num_q_heads: int, num_kv_heads: i
                        q_len=int(q_len))
 
 
+def make_new_tokens(batch: int, q_len: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                    seed=0, scale: float = 3.0) -> dict:
+    """Pre-norm q, k and v of a step's new tokens ([B, L, H, D] bf16 bits drawn from
+    N(0, scale^2)) and per-channel norm weights for q, k and v ([D] fp32, uniform in [0.5, 1.5]).
+    Inputs of the QK-norm + RoPE + append step."""
+    rq, rk, rv, rw = (np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(4))
+    shape = lambda h: (batch, q_len, h, head_dim)
+    draw = lambda r, h: f32_to_bf16_bits(np.float32(scale) * r.standard_normal(shape(h),
+                                                                                dtype=np.float32))
+    w = rw.uniform(0.5, 1.5, (3, head_dim)).astype(np.float32)
+    return dict(q=draw(rq, num_q_heads), k=draw(rk, num_kv_heads), v=draw(rv, num_kv_heads),
+                q_weight=w[0], k_weight=w[1], v_weight=w[2])
+
+
 def workload_ctx_lens(wl: Workload) -> np.ndarray:
     if isinstance(wl.ctx, str):
         rng = np.random.default_rng(np.random.SeedSequence([wl.index, 99]))

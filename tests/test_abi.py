@@ -240,11 +240,59 @@ def test_append_validation(lib):
         ERR_PLAN
 
 
+def test_rope_entry_validation(lib):
+    """decode_attn_rope_cache and decode_attn_append_kv_rope reject bad arguments on the host."""
+    c = lib.decode_attn_rope_cache
+    assert c(None, 16, 64, 0, 1e4, None) == ERR_NULL
+    assert c(A + 2, 16, 64, 0, 1e4, None) == ERR_ALIGN
+    for mp, r, fd, th in ((0, 64, 0, 1e4), (16, 63, 0, 1e4), (16, 0, 0, 1e4), (16, 64, -1, 1e4),
+                          (16, 64, 0, 0.0), (16, 64, 0, -5.0), (16, 64, 0, math.inf),
+                          (16, 64, 0, math.nan)):
+        assert c(A, mp, r, fd, th, None) == ERR_SHAPE, (mp, r, fd, th)
+    p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600)
+    bp = ctypes.byref(p)
+    f = lib.decode_attn_append_kv_rope
+
+    def call(**kw):
+        a = dict(q=A, q_out=A, k_new=A, v_new=A, k_pool=A, v_pool=A + 64, bt=A, ctx=A, batch=1,
+                 cs=A, max_pos=4096, rot=512, inter=0, flags=3, qw=A, kw=A, vw=A, eps=1e-6)
+        a.update(kw)
+        return f(bp, a["q"], a["q_out"], a["k_new"], a["v_new"], a["k_pool"], a["v_pool"], a["bt"],
+                 a["ctx"], a["batch"], a["cs"], a["max_pos"], a["rot"], a["inter"], a["flags"],
+                 a["qw"], a["kw"], a["vw"], a["eps"], None)
+
+    assert call(batch=3) == ERR_SHAPE
+    assert call(batch=-1) == ERR_SHAPE
+    assert call(rot=513) == ERR_SHAPE      # odd
+    assert call(rot=514) == ERR_SHAPE      # past D
+    assert call(rot=-2) == ERR_SHAPE
+    assert call(max_pos=0) == ERR_SHAPE
+    assert call(inter=2) == ERR_SHAPE
+    assert call(flags=4) == ERR_SHAPE
+    assert call(eps=0.0) == ERR_SHAPE
+    assert call(eps=math.nan) == ERR_SHAPE
+    assert call(batch=0) == OK             # nothing to do, nothing launched
+    assert call(q=None) == ERR_NULL
+    assert call(q_out=None) == ERR_NULL
+    assert call(k_new=None) == ERR_NULL
+    assert call(v_new=None) == ERR_NULL    # separate pools need v_new
+    assert call(cs=None) == ERR_NULL       # a rotation needs the table
+    assert call(bt=None) == ERR_NULL
+    assert call(q_out=A + 2) == ERR_ALIGN
+    assert call(v_new=A + 8) == ERR_ALIGN
+    assert call(cs=A + 2) == ERR_ALIGN
+    assert call(kw=A + 1) == ERR_ALIGN
+    bad = binding.Plan.from_buffer_copy(p)
+    bad.magic = 1
+    assert f(ctypes.byref(bad), A, A, A, A, A, A + 64, A, A, 1, A, 16, 64, 0, 0, None, None, None,
+             1e-6, None) == ERR_PLAN
+
+
 def test_status_strings(lib):
     for code in range(8):
         assert binding.decode_attn_status_str(code).startswith(binding.STATUS_NAMES[code])
     assert "unknown" in binding.decode_attn_status_str(99)
-    assert binding.decode_attn_version() == binding.ABI_VERSION == 201
+    assert binding.decode_attn_version() == binding.ABI_VERSION == 202
 
 
 def test_binding_rejects_tensors_smaller_than_the_plan():
