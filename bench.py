@@ -94,10 +94,16 @@ def main() -> int:
                     help="untimed steps for this long before the warmup steps (clock ramp-up)")
     ap.add_argument("--append", action="store_true",
                     help="each layer call first appends the step's new tokens' K/V to the pools")
+    ap.add_argument("--rope", action="store_true",
+                    help="each layer call first runs the fused QK-norm + RoPE + paged append of the "
+                         "step's new tokens, then attends with the rotated q")
     ap.add_argument("--sink", type=int, default=0,
                     help="sink keys the sliding layer also attends (StreamingLLM-style view)")
     args = ap.parse_args()
 
+    if args.append and args.rope:
+        print("--append and --rope are alternatives (--rope appends too)", flush=True)
+        return 2
     if args.gpus != 1:
         print("bench.py measures a single GPU; --gpus %d is not supported (the decode-attention "
               "path has no cross-GPU step; run with --gpus 1)" % args.gpus, flush=True)
@@ -152,14 +158,36 @@ def main() -> int:
             inp.v_pool = inp.k_pool
         k0 = bf(inp.k_pool)
         v0 = k0 if args.k_eq_v else bf(inp.v_pool)
-        ks, vs = [k0], [v0]
-        for _ in range(1, copies):
-            ks.append(k0.clone())
-            vs.append(ks[-1] if args.k_eq_v else v0.clone())
         plan = pda.decode_attn_plan(d["B"], d["Hq"], d["Hkv"], d["D"], d["S"], d["M"], d["P"],
                                     max_ctx_len=int(inp.ctx_lens.max()), window=inp.window,
                                     values_are_keys=args.k_eq_v, sink=sink, q_len=args.q_len)
         spec = wl.layers[kind]
+        rope = None
+        if args.rope:
+            # Pre-norm q, k and v of the step's new tokens, RMSNorm weights and the rotation table
+            # (full rotation, NeoX pairs; theta 1e6 for the global layer, 1e4 for the sliding one).
+            # The step is run once before the pool copies are made, so every copy already holds
+            # the rotated keys the timed steps write again.
+            new = wl_mod.make_new_tokens(d["B"], args.q_len, d["Hq"], d["Hkv"], d["D"],
+                                         seed=[wl.index, 0 if kind == "global" else 1, 7])
+            theta = 1e6 if kind == "global" else 1e4
+            max_pos = int(inp.ctx_lens.max()) + 1
+            cs = torch.empty((max_pos, d["D"]), dtype=torch.float32, device=dev)
+            pda.decode_attn_rope_cache(cs, max_pos, d["D"], theta)
+            f32 = lambda a: torch.from_numpy(a).to(dev)
+            rope = dict(new=new, theta=theta, max_pos=max_pos, cs=cs, q=bf(new["q"]),
+                        k=bf(new["k"]), v=None if args.k_eq_v else bf(new["v"]),
+                        qw=f32(new["q_weight"]), kw=f32(new["k_weight"]), eps=1e-6)
+            rope["q_out"] = torch.empty_like(rope["q"])
+            pda.decode_attn_append_kv_rope(plan, rope["q"], rope["q_out"], rope["k"], rope["v"],
+                                           k0, v0, torch.from_numpy(inp.block_table).to(dev),
+                                           torch.from_numpy(inp.ctx_lens).to(dev), d["B"], cs,
+                                           max_pos, d["D"], False, pda.NORM_QK, rope["qw"],
+                                           rope["kw"], None, rope["eps"])
+        ks, vs = [k0], [v0]
+        for _ in range(1, copies):
+            ks.append(k0.clone())
+            vs.append(ks[-1] if args.k_eq_v else v0.clone())
         # The newest q_len tokens' K/V as the append's input: the values already in the pools, so the
         # appended cache (and the oracle check) is unchanged while the copy does its full work.
         S, Lq = d["S"], args.q_len
@@ -167,11 +195,17 @@ def main() -> int:
         pages = inp.block_table[np.arange(d["B"])[:, None], pos // S]
         k_new = np.ascontiguousarray(inp.k_pool[pages, :, pos % S, :])  # [B, L, Hkv, D]
         v_new = np.ascontiguousarray(inp.v_pool[pages, :, pos % S, :])
+        # Per new token: q read and written, k (and v) read and written to its slot, one table row.
+        rope_bytes = (d["B"] * Lq * (4 * d["Hq"] * d["D"] + 4 * d["Hkv"] * d["D"] *
+                                     (1 if args.k_eq_v else 2) + 4 * d["D"]))
         layers.append(dict(
             spec=wl.layers[kind], sink=sink,
             k_new=bf(k_new), v_new=bf(v_new),
-            append_bytes=2 * k_new.size * 2 * (1 if args.k_eq_v else 2),
-            kind=kind, inp=inp, dims=d, plan=plan, q=bf(inp.q), k=ks, v=vs,
+            append_bytes=(rope_bytes if args.rope else
+                          2 * k_new.size * 2 * (1 if args.k_eq_v else 2)),
+            rope=rope,
+            kind=kind, inp=inp, dims=d, plan=plan,
+            q=rope["q_out"] if rope else bf(inp.q), k=ks, v=vs,
             bt=torch.from_numpy(inp.block_table).to(dev),
             ctx=torch.from_numpy(inp.ctx_lens).to(dev),
             out=torch.empty(lead + (d["Hq"], d["D"]), device=dev),
@@ -191,12 +225,22 @@ def main() -> int:
     B = dominant["plan"].problem.batch
 
     def append(L, r):
-        pda.decode_attn_append_kv(L["plan"], L["k_new"], L["v_new"], L["k"][r], L["v"][r],
-                                  L["bt"], L["ctx"], L["plan"].problem.batch)
+        ro = L["rope"]
+        if ro is not None:
+            pda.decode_attn_append_kv_rope(
+                L["plan"], ro["q"], ro["q_out"], ro["k"], ro["v"], L["k"][r], L["v"][r], L["bt"],
+                L["ctx"], L["plan"].problem.batch, ro["cs"], ro["max_pos"],
+                L["plan"].problem.head_dim, False, pda.NORM_QK, ro["qw"], ro["kw"], None,
+                ro["eps"])
+        else:
+            pda.decode_attn_append_kv(L["plan"], L["k_new"], L["v_new"], L["k"][r], L["v"][r],
+                                      L["bt"], L["ctx"], L["plan"].problem.batch)
+
+    appends = args.append or args.rope
 
     def run_layer(L, r, ev_s1=None):
         p = L["plan"]
-        if args.append:
+        if appends:
             append(L, r)
         if L is dominant and p.num_splits == 1:
             # One split: the layer call is stage 1 alone, writing out and lse in place.
@@ -277,7 +321,7 @@ def main() -> int:
         us = timed_calls(L, 50, flush=True)
         hot = timed_calls(L, 50, flush=False)
         med = us[len(us) // 2]
-        if args.append:
+        if appends:
             eva = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(20)]
             for i, (ea, eb) in enumerate(eva):
@@ -294,10 +338,12 @@ def main() -> int:
                              "GB_per_s": round(L["bytes"] / (med * 1e-6) / 1e9, 1),
                              "pct_of_hbm_peak": round(100 * L["bytes"] / (med * 1e-6) / 1e9 /
                                                       PEAK_HBM_GBS, 2)}
-        if args.append:
+        if appends:
             detail[L["kind"]].update(append_us_median=round(L["append_us"], 2),
-                                     append_bytes=L["append_bytes"])
-    step_bytes = sum(L["bytes"] + (L["append_bytes"] if args.append else 0) for L in layers)
+                                     append_bytes=L["append_bytes"],
+                                     append_GB_per_s=round(L["append_bytes"] /
+                                                           (L["append_us"] * 1e-6) / 1e9, 1))
+    step_bytes = sum(L["bytes"] + (L["append_bytes"] if appends else 0) for L in layers)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     s1_ms = [a.elapsed_time(b) for a, b in ev]
     s1_avg_us = 1e3 * sum(s1_ms) / len(s1_ms)
@@ -366,7 +412,8 @@ def main() -> int:
             "k_eq_v": bool(args.k_eq_v),
             "q_len": args.q_len,
             "sliding_sink": args.sink,
-            "append_in_step": bool(args.append),
+            "append_in_step": bool(appends),
+            "qk_norm_rope_in_step": bool(args.rope),
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
@@ -384,6 +431,18 @@ def main() -> int:
             for h in host:
                 h.v_pool = h.k_pool
         Lq = args.q_len
+        if args.rope:
+            # The step before attention, by the oracle, once and untimed (its arithmetic is under
+            # 0.1% of the attention's): rotated q and the appended keys.
+            from oracle import rope as orope
+            for h, L in zip(host, layers):
+                ro = L["rope"]
+                n = ro["new"]
+                qb = orope.prepare_and_append(
+                    n["q"], n["k"], None if args.k_eq_v else n["v"], h.k_pool, h.v_pool,
+                    h.block_table, h.ctx_lens, ro["max_pos"], True, False, n["q_weight"],
+                    n["k_weight"], None, ro["eps"], ro["theta"], h.k_pool.shape[-1], False)
+                h.q = qb if Lq > 1 else qb[:, 0]
 
         # A bounded sample: the whole step when its flops are within budget, else the last k of
         # the L query tokens of every sequence (exactly those queries' outputs; the oracle's time
@@ -408,6 +467,8 @@ def main() -> int:
             return refs
 
         def describe(reps, k, what):
+            if args.rope:
+                what += "; the QK-norm + RoPE + append step run once by the oracle, untimed"
             if k == Lq:
                 return "%d full %s steps (all layers), fp64 oracle, %s" % (reps, args.workload,
                                                                             what)

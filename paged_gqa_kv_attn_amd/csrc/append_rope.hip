@@ -8,12 +8,13 @@
 // sits between them (section "自定义 Inductor 融合 pass"), and fuse the q/k RMSNorm with RoPE in
 // place for both pairings, NeoX halves and GPT-J interleaved pairs (section "内核框架（Helion）").
 //
-// Layout of the work: one wave per (new token, row), a row being a q head, a new k head or a new
-// v head; four waves per workgroup, the workgroups of one token along grid.y. Each lane holds
-// D / 64 consecutive elements of its row (one 16-byte load at D = 512, 8 bytes at D = 256), so a
-// row is one coalesced read and one coalesced write. The RMS is a wave reduction; the NeoX pair
-// partner (element d +- R/2, held by another lane) comes through a per-wave LDS row, the
-// interleaved partner is in the same lane. Arithmetic is fp32 and each result is rounded once to
+// Layout of the work: a row is a q head, a new k head or a new v head of one new token; a wave
+// takes four consecutive rows of a token, four waves per workgroup, the workgroups of one token
+// along grid.y. Each lane holds D / 64 consecutive elements of a row (one 16-byte load at D = 512,
+// 8 bytes at D = 256), so a row is one coalesced read and one coalesced write, and a wave keeps
+// four rows' loads in flight at once. The RMS is a wave reduction; the NeoX pair partner (element
+// d +- R/2, held by another lane) comes through the wave's LDS rows, the interleaved partner is in
+// the same lane. Arithmetic is fp32 and each result is rounded once to
 // bf16 (nearest even). The rotation table (cos and sin per position and pair, fp32) is built
 // once per layer configuration by rope_cache_kernel in double precision.
 
@@ -26,6 +27,7 @@ namespace decode_attn {
 namespace {
 
 constexpr int kRopeWaves = 4;
+constexpr int kRopeRowsPerWave = 4;
 
 __global__ __launch_bounds__(256) void rope_cache_kernel(float* cos_sin, int64_t count,
                                                          int rotary_dim, int freq_dim,
@@ -55,121 +57,256 @@ struct RowVec<8> {
   typedef u32x4 type;  // 8 bf16
 };
 
-template <int D>
-__global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a) {
-  constexpr int E = D / 64;
-  typedef typename RowVec<E>::type vec_t;
-  __shared__ float rows[kRopeWaves][D];
+// The lane's E consecutive floats of p (all 1 when p is NULL). FAST: p + lane * E is 16-byte
+// aligned and the values come in as vector loads.
+template <int N>
+__device__ __forceinline__ void load_floats(const float* p, float* v) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int n = 0; n < N; n += 4) {
+      const f32x4 w = *reinterpret_cast<const f32x4*>(p + n);
+      v[n] = w[0];
+      v[n + 1] = w[1];
+      v[n + 2] = w[2];
+      v[n + 3] = w[3];
+    }
+  } else {
+    static_assert(N == 2, "two or a multiple of four floats");
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 w = *reinterpret_cast<const f32x2*>(p);
+    v[0] = w[0];
+    v[1] = w[1];
+  }
+}
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int tok = blockIdx.x;  // b * L + i
-  const int b = tok / a.q_len;
-  const int i = tok - b * a.q_len;
-  const int t = a.ctx_lens[b] - a.q_len + i;
-  if (t < 0 || t >= a.max_position) return;  // the same for the whole workgroup
+template <int E, bool FAST>
+__device__ __forceinline__ void load_weights(const float* w, int lane, float* v) {
+  if (!w) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = 1.f;
+  } else if (FAST) {
+    load_floats<E>(w + lane * E, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = w[lane * E + e];
+  }
+}
 
+// Where a row comes from and goes to; kind -1 = nothing to do (past the token's rows, or a k/v row
+// whose slot is skipped).
+struct RowRef {
+  const uint16_t* src;
+  uint16_t* dst;
+  int kind;  // 0 = q head, 1 = new k head, 2 = new v head
+};
+
+__device__ __forceinline__ RowRef row_ref(const AppendRopeArgs& a, int r, int tok, int b, int t,
+                                          int rows_per_token, int D) {
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
-  const bool same = a.v_pool == a.k_pool;
-  const int rows_per_token = Hq + Hkv * (same ? 1 : 2);
-  const int r = blockIdx.y * kRopeWaves + wave;
-
-  const uint16_t* src = nullptr;
-  uint16_t* dst = nullptr;
-  const float* weight = nullptr;
-  bool norm = false, rotate = false;
+  RowRef ref{nullptr, nullptr, -1};
   if (r < Hq) {
-    src = a.q + ((size_t)tok * Hq + r) * D;
-    dst = a.q_out + ((size_t)tok * Hq + r) * D;
-    weight = a.q_weight;
-    norm = a.norm_flags & 1;
-    rotate = true;
+    ref.src = a.q + ((size_t)tok * Hq + r) * D;
+    ref.dst = a.q_out + ((size_t)tok * Hq + r) * D;
+    ref.kind = 0;
   } else if (r < rows_per_token) {
     const bool is_v = r - Hq >= Hkv;
     const int g = is_v ? r - Hq - Hkv : r - Hq;
     const int col = t / a.page_size;
-    const int page = col < a.max_pages_per_seq
-                         ? a.block_table[(size_t)b * a.max_pages_per_seq + col]
-                         : -1;
+    const int page =
+        col < a.max_pages_per_seq ? load_uniform(a.block_table, (size_t)b * a.max_pages_per_seq + col)
+                                  : -1;
     if ((unsigned)page < (unsigned)a.num_pages) {
-      const size_t slot =
-          (((size_t)page * Hkv + g) * a.page_size + (t - col * a.page_size)) * D;
-      dst = (is_v ? a.v_pool : a.k_pool) + slot;
-      src = (is_v ? a.v_new : a.k_new) + ((size_t)tok * Hkv + g) * D;
-      weight = is_v ? a.v_weight : a.k_weight;
-      norm = is_v ? (a.norm_flags & 2) : (a.norm_flags & 1);
-      rotate = !is_v;
+      const size_t slot = (((size_t)page * Hkv + g) * a.page_size + (t - col * a.page_size)) * D;
+      ref.dst = (is_v ? a.v_pool : a.k_pool) + slot;
+      ref.src = (is_v ? a.v_new : a.k_new) + ((size_t)tok * Hkv + g) * D;
+      ref.kind = is_v ? 2 : 1;
     }
   }
-  const bool active = dst != nullptr;  // the same for the whole wave
+  return ref;
+}
 
-  float x[E];
-  if (active) {
-    const vec_t raw = reinterpret_cast<const vec_t*>(src)[lane];
-#pragma unroll
-    for (int e = 0; e < E; e += 2) {
-      const uint32_t w2 = raw[e / 2];
-      x[e] = __builtin_bit_cast(float, w2 << 16);
-      x[e + 1] = __builtin_bit_cast(float, w2 & 0xFFFF0000u);
-    }
-    if (norm) {
-      float ss = 0.f;
-#pragma unroll
-      for (int e = 0; e < E; ++e) ss += x[e] * x[e];
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) ss += __shfl_xor(ss, m);
-      const float inv = 1.0f / sqrtf(ss * (1.0f / D) + a.eps);
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        x[e] *= inv;
-        if (weight) x[e] *= weight[lane * E + e];
-      }
-    }
-  }
+// One workgroup per (new token, 4 * RW rows); wave w takes rows RW * w .. RW * w + RW - 1 of the
+// workgroup's slice. Every global load of a wave (its RW rows, the norm weights, its lanes' cos
+// and sin) is issued before any result is needed, so one memory latency covers the wave's work.
+//
+// FAST (chosen on the host when R is a multiple of 2 * D / 64 and the table and weights are
+// 16-byte aligned): a lane's elements are all rotated or all not, and for NeoX all on one side of
+// R/2, so the lane's weights and cos / sin come in as vector loads and the NeoX partner is the
+// same element of lane +- R / (2 E), fetched with a cross-lane permute (no LDS, no barrier).
+// Otherwise the general path: per-element table loads and the partner through LDS.
+template <int D, int RW, bool FAST>
+__global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a) {
+  constexpr int E = D / 64;
+  typedef typename RowVec<E>::type vec_t;
+  __shared__ float rows[FAST ? 1 : kRopeWaves][FAST ? 1 : RW][FAST ? 1 : D];
 
+  const int lane = threadIdx.x & 63;
+  // The wave index is the same in all lanes; readfirstlane lets the row bookkeeping below stay in
+  // scalar registers and scalar branches.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok = blockIdx.x;  // b * L + i
+  const int b = tok / a.q_len;
+  const int i = tok - b * a.q_len;
+  const int t = load_uniform(a.ctx_lens, b) - a.q_len + i;
+  if (t < 0 || t >= a.max_position) return;  // the same for the whole workgroup
+
+  const bool same = a.v_pool == a.k_pool;
+  const int rows_per_token = a.num_q_heads + a.num_kv_heads * (same ? 1 : 2);
+  const int r0 = (blockIdx.y * kRopeWaves + wave) * RW;
   const int R = a.rotary_dim;
   const int half = R / 2;
+
+  RowRef ref[RW];
+#pragma unroll
+  for (int k = 0; k < RW; ++k) ref[k] = row_ref(a, r0 + k, tok, b, t, rows_per_token, D);
+  // All RW loads go out back to back; a row with nothing to do reads this token's first q head
+  // (always in bounds) and its result is dropped.
+  const uint16_t* const spare = a.q + (size_t)tok * a.num_q_heads * D;
+  vec_t raw[RW];
+#pragma unroll
+  for (int k = 0; k < RW; ++k)
+    raw[k] = reinterpret_cast<const vec_t*>(ref[k].kind >= 0 ? ref[k].src : spare)[lane];
+  bool has_q = false, has_k = false, has_v = false;  // row kinds present in this wave
+#pragma unroll
+  for (int k = 0; k < RW; ++k) {
+    has_q |= ref[k].kind == 0;
+    has_k |= ref[k].kind == 1;
+    has_v |= ref[k].kind == 2;
+  }
+  const bool norm_qk = a.norm_flags & 1, norm_v = a.norm_flags & 2;
+  float wq[E], wk[E], wv[E], cv[E], sv[E];
+  load_weights<E, FAST>((norm_qk && has_q) ? a.q_weight : nullptr, lane, wq);
+  load_weights<E, FAST>((norm_qk && has_k) ? a.k_weight : nullptr, lane, wk);
+  load_weights<E, FAST>((norm_v && has_v) ? a.v_weight : nullptr, lane, wv);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    cv[e] = 1.f;
+    sv[e] = 0.f;
+  }
+  const bool rotates = R > 0 && (has_q || has_k);
   const float* cs = a.cos_sin + (size_t)t * R;
-  if (R > 0 && !a.interleaved) {
-    // NeoX pairs (d, d + R/2): the partner sits in another lane, so the row goes through LDS.
-    if (active && rotate) {
+  if (FAST && rotates) {
+    if (lane * E < R) {
+      if (a.interleaved) {
+        // pairs (2j, 2j + 1): the lane's E / 2 pairs start at j = lane * E / 2.
+        float c[E / 2], sn[E / 2];
+        load_floats<E / 2>(cs + lane * E / 2, c);
+        load_floats<E / 2>(cs + half + lane * E / 2, sn);
 #pragma unroll
-      for (int e = 0; e < E; ++e) rows[wave][lane * E + e] = x[e];
-    }
-    __syncthreads();
-    if (active && rotate) {
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int d = lane * E + e;
-        if (d < R) {
-          const bool lo = d < half;
-          const int j = lo ? d : d - half;
-          const float p = rows[wave][lo ? d + half : j];
-          const float c = cs[j], s = cs[half + j];
-          x[e] = lo ? x[e] * c - p * s : x[e] * c + p * s;
+        for (int e = 0; e < E; ++e) {
+          cv[e] = c[e / 2];
+          sv[e] = sn[e / 2];
         }
+      } else {
+        const int j0 = lane * E < half ? lane * E : lane * E - half;
+        load_floats<E>(cs + j0, cv);
+        load_floats<E>(cs + half + j0, sv);
       }
     }
-  } else if (R > 0 && active && rotate) {
-    // GPT-J pairs (2j, 2j + 1): both elements are in this lane (E is even).
+  } else if (rotates) {
 #pragma unroll
-    for (int e = 0; e < E; e += 2) {
+    for (int e = 0; e < E; ++e) {
+      // Lanes past the rotated dims read pair 0 and keep the identity rotation.
       const int d = lane * E + e;
-      if (d < R) {
-        const int j = d / 2;
-        const float c = cs[j], s = cs[half + j];
-        const float x1 = x[e], x2 = x[e + 1];
-        x[e] = x1 * c - x2 * s;
-        x[e + 1] = x2 * c + x1 * s;
-      }
+      const int j = d >= R ? 0 : a.interleaved ? d / 2 : (d < half ? d : d - half);
+      const float c = cs[j], sn = cs[half + j];
+      cv[e] = d < R ? c : 1.f;
+      sv[e] = d < R ? sn : 0.f;
     }
   }
 
-  if (active) {
+  float x[RW][E];
+#pragma unroll
+  for (int k = 0; k < RW; ++k) {
+#pragma unroll
+    for (int e = 0; e < E; e += 2) {
+      const uint32_t w2 = raw[k][e / 2];
+      x[k][e] = __builtin_bit_cast(float, w2 << 16);
+      x[k][e + 1] = __builtin_bit_cast(float, w2 & 0xFFFF0000u);
+    }
+  }
+  // RMSNorm: the RW rows' sums of squares reduce across the wave side by side.
+  float ss[RW];
+#pragma unroll
+  for (int k = 0; k < RW; ++k) {
+    ss[k] = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) ss[k] += x[k][e] * x[k][e];
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+#pragma unroll
+    for (int k = 0; k < RW; ++k) ss[k] += __shfl_xor(ss[k], m);
+  }
+#pragma unroll
+  for (int k = 0; k < RW; ++k) {
+    const int kind = ref[k].kind;
+    if ((kind <= 1 && kind >= 0 && norm_qk) || (kind == 2 && norm_v)) {
+      const float inv = 1.0f / sqrtf(ss[k] * (1.0f / D) + a.eps);
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        x[k][e] = x[k][e] * inv * (kind == 0 ? wq[e] : kind == 1 ? wk[e] : wv[e]);
+    }
+  }
+
+  if (FAST && R > 0 && !a.interleaved) {
+    // NeoX pairs (d, d + R/2): element e of lane l pairs with element e of lane l +- R / (2E).
+    const int off = half / E;
+    const bool lo = lane * E < half;
+    const int partner = lane * E >= R ? lane : lo ? lane + off : lane - off;
+    const float sign = lo ? -1.f : 1.f;
+#pragma unroll
+    for (int k = 0; k < RW; ++k)
+      if (ref[k].kind == 0 || ref[k].kind == 1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float p = __shfl(x[k][e], partner);
+          x[k][e] = x[k][e] * cv[e] + sign * (p * sv[e]);
+        }
+      }
+  } else if (R > 0 && !a.interleaved) {
+    // NeoX pairs (d, d + R/2): the partner sits in another lane, so the rows go through LDS.
+#pragma unroll
+    for (int k = 0; k < RW; ++k)
+      if (ref[k].kind == 0 || ref[k].kind == 1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) rows[wave][k][lane * E + e] = x[k][e];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < RW; ++k)
+      if (ref[k].kind == 0 || ref[k].kind == 1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int d = lane * E + e;
+          if (d < R) {
+            const bool lo = d < half;
+            const float p = rows[wave][k][lo ? d + half : d - half];
+            x[k][e] = lo ? x[k][e] * cv[e] - p * sv[e] : x[k][e] * cv[e] + p * sv[e];
+          }
+        }
+      }
+  } else if (R > 0) {
+    // GPT-J pairs (2j, 2j + 1): both elements are in this lane (E is even).
+#pragma unroll
+    for (int k = 0; k < RW; ++k)
+      if (ref[k].kind == 0 || ref[k].kind == 1) {
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          const float x1 = x[k][e], x2 = x[k][e + 1];
+          x[k][e] = x1 * cv[e] - x2 * sv[e];
+          x[k][e + 1] = x2 * cv[e] + x1 * sv[e];
+        }
+      }
+  }
+
+#pragma unroll
+  for (int k = 0; k < RW; ++k) {
+    if (ref[k].kind < 0) continue;
     vec_t out;
 #pragma unroll
-    for (int e = 0; e < E; e += 2) out[e / 2] = pack_bf16x2(x[e], x[e + 1]);
-    reinterpret_cast<vec_t*>(dst)[lane] = out;
+    for (int e = 0; e < E; e += 2) out[e / 2] = pack_bf16x2(x[k][e], x[k][e + 1]);
+    reinterpret_cast<vec_t*>(ref[k].dst)[lane] = out;
   }
 }
 
@@ -188,11 +325,20 @@ hipError_t launch_rope_cache(float* cos_sin, int max_position, int rotary_dim, i
 hipError_t launch_append_rope(const AppendRopeArgs& args, int head_dim, int batch,
                               hipStream_t stream) {
   const int rows = args.num_q_heads + args.num_kv_heads * (args.v_pool == args.k_pool ? 1 : 2);
-  dim3 grid(batch * args.q_len, (rows + kRopeWaves - 1) / kRopeWaves);
+  constexpr int per_block = kRopeWaves * kRopeRowsPerWave;
+  dim3 grid(batch * args.q_len, (rows + per_block - 1) / per_block);
   dim3 block(64 * kRopeWaves);
   void* kargs[] = {const_cast<AppendRopeArgs*>(&args)};
-  const void* fn = head_dim == 512 ? reinterpret_cast<const void*>(&append_rope_kernel<512>)
-                                   : reinterpret_cast<const void*>(&append_rope_kernel<256>);
+  const auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  const bool fast = args.rotary_dim % (2 * (head_dim / 64)) == 0 && a16(args.cos_sin) &&
+                    a16(args.q_weight) && a16(args.k_weight) && a16(args.v_weight);
+  constexpr int RW = kRopeRowsPerWave;
+  const void* fn =
+      head_dim == 512
+          ? (fast ? reinterpret_cast<const void*>(&append_rope_kernel<512, RW, true>)
+                  : reinterpret_cast<const void*>(&append_rope_kernel<512, RW, false>))
+          : (fast ? reinterpret_cast<const void*>(&append_rope_kernel<256, RW, true>)
+                  : reinterpret_cast<const void*>(&append_rope_kernel<256, RW, false>));
   return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
 }
 

@@ -106,9 +106,18 @@ def _written_slots(inp, ctx, L, max_position, pool_shape):
     return out
 
 
+def _f32_offset(a, misalign):
+    """a on the device; with misalign, as a view 4 bytes past a 16-byte boundary."""
+    if not misalign:
+        return _f32(a)
+    flat = np.ascontiguousarray(a, dtype=np.float32).ravel()
+    big = _f32(np.concatenate([np.zeros(1, np.float32), flat]))
+    return big[1:].view(a.shape)
+
+
 def run_case(D, Hq, Hkv, S, ctx, L, rot, interleaved, norm_qk, norm_v, same_pool, seed,
              max_position=None, freq_dim=0, theta=1e4, batch=None, in_place=False,
-             weights=True, pool=None):
+             weights=True, pool=None, misalign=False):
     """One fused step on the GPU and in the oracle; checks q_out and both pools. Returns the GPU
     buffers, the oracle's q bits and pools, and the step's inputs for an attention check."""
     torch = _torch()
@@ -133,14 +142,15 @@ def run_case(D, Hq, Hkv, S, ctx, L, rot, interleaved, norm_qk, norm_v, same_pool
     q_out = q_dev if in_place else _bf(np.full(new["q"].shape, NAN_BITS, np.uint16))
     cs = None
     if rot > 0:
-        cs = torch.empty((max_position, rot), dtype=torch.float32, device=gu.device())
+        cs = _f32_offset(np.zeros((max_position, rot), np.float32), misalign)
         pda.decode_attn_rope_cache(cs, max_position, rot, theta, freq_dim)
     plan = gu.make_plan(inp, q_len=L) if pool is None else gu.make_plan(inp)
     pda.decode_attn_append_kv_rope(
         plan, q_dev, q_out, _bf(new["k"]), None if same_pool else _bf(new["v"]), t["k"], t["v"],
         t["bt"], t["ctx"], batch, cs, max_position, rot, interleaved, flags,
-        _f32(qw) if qw is not None else None, _f32(kw) if kw is not None else None,
-        _f32(vw) if vw is not None else None, 1e-6)
+        _f32_offset(qw, misalign) if qw is not None else None,
+        _f32_offset(kw, misalign) if kw is not None else None,
+        _f32_offset(vw, misalign) if vw is not None else None, 1e-6)
     torch.cuda.synchronize()
 
     # Oracle on the first `batch` sequences.
@@ -221,6 +231,19 @@ def test_append_kv_rope_norm_modes(norm_qk, norm_v, weights):
     print("rope norm qk=%d v=%d w=%d" % (norm_qk, norm_v, weights), flush=True)
     run_case(256, 16, 8, 16, [40, 1, 777], 3, 256, False, norm_qk, norm_v, False,
              seed=[81, norm_qk, norm_v, weights], weights=weights)
+
+
+@pytest.mark.parametrize("D,rot,interleaved,misalign", [
+    (512, 40, False, False), (512, 2, True, False), (256, 36, False, False),
+    (256, 12, True, False), (256, 256, True, True), (512, 512, False, True),
+    (512, 128, False, True)])
+def test_append_kv_rope_general_path(D, rot, interleaved, misalign):
+    """The per-element path: rotated widths that split a lane's elements (R not a multiple of
+    2 * D / 64) or a table and weights only 4-byte aligned."""
+    print("rope general D=%d R=%d il=%d mis=%d" % (D, rot, interleaved, misalign), flush=True)
+    Hq, Hkv = (16, 2) if D == 512 else (16, 8)
+    run_case(D, Hq, Hkv, 16, [9, 260, 1], 3, rot, interleaved, True, True, False,
+             seed=[88, D, rot, int(interleaved), int(misalign)], misalign=misalign)
 
 
 def test_append_kv_rope_no_rotation_and_in_place():
