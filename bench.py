@@ -120,11 +120,18 @@ def main() -> int:
         n = 1 << 30
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(5):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(5)]
+        for ea, eb in evs:
+            ea.record(stream)
             dst.copy_(src)
+            eb.record(stream)
         torch.cuda.synchronize()
+        us = sorted(1e3 * ea.elapsed_time(eb) for ea, eb in evs)
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
-                          "launches": 5}), flush=True)
+                          "launches": 5, "median_us": round(us[2], 1),
+                          "read_plus_write_GB_per_s": round(2 * n / (us[2] * 1e-6) / 1e9, 1)}),
+              flush=True)
         return 0
 
     import paged_gqa_kv_attn_amd as pda
