@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 
 import gpu_util as gu
+import oracle
 from oracle import rope as orope
 import paged_gqa_kv_attn_amd as pda
 from paged_gqa_kv_attn_amd.workloads import (WORKLOADS, make_layer_inputs, make_new_tokens,
@@ -319,3 +320,80 @@ def test_append_kv_rope_workload_global(L):
     inp.k_pool, inp.v_pool = r["k_ref"], r["v_ref"]
     err, cos = gu.compare(out, lse, *gu.reference(inp), "rope+attend long_ctx L%d" % L)
     print("  max_abs_err %.3g  min_cos %.7f" % (err, cos), flush=True)
+
+
+def test_decode_loop_in_a_graph():
+    """A decode loop: the fused step then attention captured once in a HIP graph; each replay
+    appends the next token of every sequence (ctx_lens advance by one through the same buffer,
+    with fresh q, k and v), and is compared bit for bit with the same calls made eagerly on a
+    second set of buffers, and with the oracle's step followed by the attention oracle."""
+    torch = _torch()
+    gu.ensure_library()
+    dev = gu.device()
+    D, Hq, Hkv, B, steps, max_pos = 512, 16, 2, 2, 4, 2048
+    ctx0 = np.array([100, 517], dtype=np.int32)
+    inp = make_layer_inputs(ctx0 + steps, Hq, Hkv, D, page_size=16, seed=90, poison=False)
+    inp.ctx_lens[:] = ctx0
+    plan = gu.make_plan(inp)
+    cs = torch.empty((max_pos, D), dtype=torch.float32, device=dev)
+    pda.decode_attn_rope_cache(cs, max_pos, D, 1e6)
+    w = make_new_tokens(B, 1, Hq, Hkv, D, seed=[91, 0])
+    wq, wk = _f32(w["q_weight"]), _f32(w["k_weight"])
+
+    def buffers():
+        t = gu.upload(inp)
+        t.update(q_raw=_bf(w["q"]), q=_bf(w["q"]), k_new=_bf(w["k"]), v_new=_bf(w["v"]),
+                 out=torch.zeros((B, Hq, D), device=dev),
+                 ws=torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev))
+        return t
+
+    def step(t):
+        pda.decode_attn_append_kv_rope(plan, t["q_raw"], t["q"], t["k_new"], t["v_new"], t["k"],
+                                       t["v"], t["bt"], t["ctx"], B, cs, max_pos, D, False,
+                                       pda.NORM_QK, wq, wk, None, 1e-6)
+        pda.decode_attn_global(plan, t["q"], t["k"], t["v"], t["bt"], t["ctx"], B, inp.scale,
+                               t["out"], None, t["ws"])
+
+    host_k, host_v = inp.k_pool.copy(), inp.v_pool.copy()
+    tg, te = buffers(), buffers()
+
+    def feed(t, new, ctx):
+        for key, src in (("q_raw", new["q"]), ("k_new", new["k"]), ("v_new", new["v"])):
+            t[key].copy_(_bf(src))
+        t["ctx"].copy_(torch.from_numpy(ctx).to(dev))
+
+    # Warm up on the capture stream with the first replay's data (the replay rewrites the same
+    # slot with the same values), then capture.
+    first = make_new_tokens(B, 1, Hq, Hkv, D, seed=[92, 0])
+    feed(tg, first, ctx0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(tg)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(tg)
+    torch.cuda.synchronize()
+
+    for it in range(steps):
+        print("graph decode step %d" % it, flush=True)
+        new = make_new_tokens(B, 1, Hq, Hkv, D, seed=[92, it])
+        ctx = (ctx0 + it).astype(np.int32)
+        feed(tg, new, ctx)
+        feed(te, new, ctx)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        step(te)
+        torch.cuda.synchronize()
+        for key in ("q", "k", "v"):
+            np.testing.assert_array_equal(_host(tg[key]), _host(te[key]), err_msg="%s %d" % (key, it))
+        got = tg["out"].cpu().numpy()
+        np.testing.assert_array_equal(got, te["out"].cpu().numpy())
+        q_bits = orope.prepare_and_append(new["q"], new["k"], new["v"], host_k, host_v,
+                                          inp.block_table, ctx, max_pos, True, False,
+                                          w["q_weight"], w["k_weight"], None, 1e-6, 1e6, D, False)
+        ref = oracle.decode_attn(q_bits[:, 0], host_k, host_v, inp.block_table, ctx, inp.scale)
+        gu.compare(got, None, *ref, "graph decode step %d" % it)
