@@ -97,6 +97,8 @@ def main() -> int:
     ap.add_argument("--rope", action="store_true",
                     help="each layer call first runs the fused QK-norm + RoPE + paged append of the "
                          "step's new tokens, then attends with the rotated q")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay diagnostic after the timed region")
     ap.add_argument("--sink", type=int, default=0,
                     help="sink keys the sliding layer also attends (StreamingLLM-style view)")
     args = ap.parse_args()
@@ -299,6 +301,38 @@ def main() -> int:
 
     ms_per_step = (t1 - t0) * 1e3 / K
 
+    # Graph replay, a diagnostic after the timed region: the same step captured once per pool copy
+    # in a HIP graph, as a serving loop runs it, which removes the host's launch gaps between the
+    # kernels. The kernels and their arguments are the eager step's.
+    graph_us = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for r in range(R):
+                for L in layers:
+                    run_layer(L, r)
+        stream.wait_stream(side)
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for L in layers:
+                    run_layer(L, r)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ga.record(stream)
+        for i in range(K):
+            graphs[i % R].replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        graph_us = 1e3 * ga.elapsed_time(gb) / K
+        del graphs
+
     # Per-layer breakdown, after (outside) the timed region: events around each layer call.
     # Cold: before every call a 512 MB buffer is written (outside the event pair), which evicts
     # the L2s and the MALL, so the call reads its K/V from HBM whatever the workload's size.
@@ -424,6 +458,11 @@ def main() -> int:
         },
         "us_per_step": round(ms_per_step * 1e3, 2),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "graph_replay": (None if graph_us is None else {
+            "us_per_step": round(graph_us, 2),
+            "GB_per_s": round(step_bytes / (graph_us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100.0 * step_bytes / (graph_us * 1e-6) / 1e9 /
+                                     PEAK_HBM_GBS, 2)}),
         "roofline": roofline,
         "cpu_baseline": None,
         "layers_detail": detail,
