@@ -92,15 +92,16 @@ __device__ __forceinline__ void load_weights(const float* w, int lane, float* v)
   }
 }
 
-// Where a row comes from and goes to; kind -1 = nothing to do (past the token's rows, or a k/v row
-// whose slot is skipped).
+// Where a row comes from and goes to. kind -1: past the token's rows (nothing to do). The source
+// does not depend on the block table, so the row loads are issued before the page id arrives; a
+// k/v row whose slot is skipped gets no destination.
 struct RowRef {
   const uint16_t* src;
   uint16_t* dst;
   int kind;  // 0 = q head, 1 = new k head, 2 = new v head
 };
 
-__device__ __forceinline__ RowRef row_ref(const AppendRopeArgs& a, int r, int tok, int b, int t,
+__device__ __forceinline__ RowRef row_src(const AppendRopeArgs& a, int r, int tok,
                                           int rows_per_token, int D) {
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   RowRef ref{nullptr, nullptr, -1};
@@ -111,18 +112,20 @@ __device__ __forceinline__ RowRef row_ref(const AppendRopeArgs& a, int r, int to
   } else if (r < rows_per_token) {
     const bool is_v = r - Hq >= Hkv;
     const int g = is_v ? r - Hq - Hkv : r - Hq;
-    const int col = t / a.page_size;
-    const int page =
-        col < a.max_pages_per_seq ? load_uniform(a.block_table, (size_t)b * a.max_pages_per_seq + col)
-                                  : -1;
-    if ((unsigned)page < (unsigned)a.num_pages) {
-      const size_t slot = (((size_t)page * Hkv + g) * a.page_size + (t - col * a.page_size)) * D;
-      ref.dst = (is_v ? a.v_pool : a.k_pool) + slot;
-      ref.src = (is_v ? a.v_new : a.k_new) + ((size_t)tok * Hkv + g) * D;
-      ref.kind = is_v ? 2 : 1;
-    }
+    ref.src = (is_v ? a.v_new : a.k_new) + ((size_t)tok * Hkv + g) * D;
+    ref.kind = is_v ? 2 : 1;
   }
   return ref;
+}
+
+// Destination of k/v row r in page `page` (the token's slot t % S), or none for an invalid page.
+__device__ __forceinline__ void row_dst(const AppendRopeArgs& a, RowRef& ref, int r, int page,
+                                        int slot, int D) {
+  if (ref.kind < 1 || (unsigned)page >= (unsigned)a.num_pages) return;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
+  const int g = ref.kind == 2 ? r - Hq - Hkv : r - Hq;
+  ref.dst = (ref.kind == 2 ? a.v_pool : a.k_pool) +
+            (((size_t)page * Hkv + g) * a.page_size + slot) * D;
 }
 
 // One workgroup per (new token, 4 * RW rows); wave w takes rows RW * w .. RW * w + RW - 1 of the
@@ -134,8 +137,9 @@ __device__ __forceinline__ RowRef row_ref(const AppendRopeArgs& a, int r, int to
 // R/2, so the lane's weights and cos / sin come in as vector loads and the NeoX partner is the
 // same element of lane +- R / (2 E), fetched with a cross-lane permute (no LDS, no barrier).
 // Otherwise the general path: per-element table loads and the partner through LDS.
-template <int D, int RW, bool FAST>
+template <int D, int RW, int MODE>
 __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a) {
+  constexpr bool FAST = MODE != 0;
   constexpr int E = D / 64;
   typedef typename RowVec<E>::type vec_t;
   __shared__ float rows[FAST ? 1 : kRopeWaves][FAST ? 1 : RW][FAST ? 1 : D];
@@ -155,10 +159,11 @@ __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a
   const int r0 = (blockIdx.y * kRopeWaves + wave) * RW;
   const int R = a.rotary_dim;
   const int half = R / 2;
+  const bool interleaved = MODE == 0 ? a.interleaved != 0 : MODE == 2;
 
   RowRef ref[RW];
 #pragma unroll
-  for (int k = 0; k < RW; ++k) ref[k] = row_ref(a, r0 + k, tok, b, t, rows_per_token, D);
+  for (int k = 0; k < RW; ++k) ref[k] = row_src(a, r0 + k, tok, rows_per_token, D);
   // All RW loads go out back to back; a row with nothing to do reads this token's first q head
   // (always in bounds) and its result is dropped.
   const uint16_t* const spare = a.q + (size_t)tok * a.num_q_heads * D;
@@ -173,6 +178,16 @@ __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a
     has_k |= ref[k].kind == 1;
     has_v |= ref[k].kind == 2;
   }
+  // The token's page (one block-table entry for all its k/v rows), read while the loads fly.
+  if (has_k || has_v) {
+    const int col = t / a.page_size;
+    const int page = col < a.max_pages_per_seq
+                         ? load_uniform(a.block_table, (size_t)b * a.max_pages_per_seq + col)
+                         : -1;
+#pragma unroll
+    for (int k = 0; k < RW; ++k) row_dst(a, ref[k], r0 + k, page, t - col * a.page_size, D);
+  }
+
   const bool norm_qk = a.norm_flags & 1, norm_v = a.norm_flags & 2;
   float wq[E], wk[E], wv[E], cv[E], sv[E];
   load_weights<E, FAST>((norm_qk && has_q) ? a.q_weight : nullptr, lane, wq);
@@ -185,30 +200,27 @@ __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a
   }
   const bool rotates = R > 0 && (has_q || has_k);
   const float* cs = a.cos_sin + (size_t)t * R;
+  const bool rot_lane = lane * E < R;  // FAST: all of the lane's elements rotate, or none
   if (FAST && rotates) {
-    if (lane * E < R) {
-      if (a.interleaved) {
-        // pairs (2j, 2j + 1): the lane's E / 2 pairs start at j = lane * E / 2.
-        float c[E / 2], sn[E / 2];
-        load_floats<E / 2>(cs + lane * E / 2, c);
-        load_floats<E / 2>(cs + half + lane * E / 2, sn);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          cv[e] = c[e / 2];
-          sv[e] = sn[e / 2];
-        }
-      } else {
-        const int j0 = lane * E < half ? lane * E : lane * E - half;
-        load_floats<E>(cs + j0, cv);
-        load_floats<E>(cs + half + j0, sv);
-      }
+    // Every lane loads (a lane past the rotated dims reads pair 0, in bounds, and drops it below),
+    // so no lane waits at a branch for the others' loads.
+    if constexpr (MODE == 2) {
+      // pairs (2j, 2j + 1): the lane's E / 2 pairs start at j = lane * E / 2; cv / sv hold
+      // one value per pair.
+      const int j0 = rot_lane ? lane * E / 2 : 0;
+      load_floats<E / 2>(cs + j0, cv);
+      load_floats<E / 2>(cs + half + j0, sv);
+    } else {
+      const int j0 = !rot_lane ? 0 : lane * E < half ? lane * E : lane * E - half;
+      load_floats<E>(cs + j0, cv);
+      load_floats<E>(cs + half + j0, sv);
     }
   } else if (rotates) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       // Lanes past the rotated dims read pair 0 and keep the identity rotation.
       const int d = lane * E + e;
-      const int j = d >= R ? 0 : a.interleaved ? d / 2 : (d < half ? d : d - half);
+      const int j = d >= R ? 0 : interleaved ? d / 2 : (d < half ? d : d - half);
       const float c = cs[j], sn = cs[half + j];
       cv[e] = d < R ? c : 1.f;
       sv[e] = d < R ? sn : 0.f;
@@ -249,7 +261,14 @@ __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a
     }
   }
 
-  if (FAST && R > 0 && !a.interleaved) {
+  if (FAST && rotates) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      cv[e] = rot_lane ? cv[e] : 1.f;
+      sv[e] = rot_lane ? sv[e] : 0.f;
+    }
+  }
+  if (FAST && R > 0 && !interleaved) {
     // NeoX pairs (d, d + R/2): element e of lane l pairs with element e of lane l +- R / (2E).
     const int off = half / E;
     const bool lo = lane * E < half;
@@ -264,7 +283,7 @@ __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a
           x[k][e] = x[k][e] * cv[e] + sign * (p * sv[e]);
         }
       }
-  } else if (R > 0 && !a.interleaved) {
+  } else if (R > 0 && !interleaved) {
     // NeoX pairs (d, d + R/2): the partner sits in another lane, so the rows go through LDS.
 #pragma unroll
     for (int k = 0; k < RW; ++k)
@@ -293,16 +312,17 @@ __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a
       if (ref[k].kind == 0 || ref[k].kind == 1) {
 #pragma unroll
         for (int e = 0; e < E; e += 2) {
+          const int j = MODE == 2 ? e / 2 : e;  // where this pair's cos / sin sit
           const float x1 = x[k][e], x2 = x[k][e + 1];
-          x[k][e] = x1 * cv[e] - x2 * sv[e];
-          x[k][e + 1] = x2 * cv[e] + x1 * sv[e];
+          x[k][e] = x1 * cv[j] - x2 * sv[j];
+          x[k][e + 1] = x2 * cv[j] + x1 * sv[j];
         }
       }
   }
 
 #pragma unroll
   for (int k = 0; k < RW; ++k) {
-    if (ref[k].kind < 0) continue;
+    if (ref[k].kind < 0 || ref[k].dst == nullptr) continue;
     vec_t out;
 #pragma unroll
     for (int e = 0; e < E; e += 2) out[e / 2] = pack_bf16x2(x[k][e], x[k][e + 1]);
@@ -333,12 +353,16 @@ hipError_t launch_append_rope(const AppendRopeArgs& args, int head_dim, int batc
   const bool fast = args.rotary_dim % (2 * (head_dim / 64)) == 0 && a16(args.cos_sin) &&
                     a16(args.q_weight) && a16(args.k_weight) && a16(args.v_weight);
   constexpr int RW = kRopeRowsPerWave;
-  const void* fn =
-      head_dim == 512
-          ? (fast ? reinterpret_cast<const void*>(&append_rope_kernel<512, RW, true>)
-                  : reinterpret_cast<const void*>(&append_rope_kernel<512, RW, false>))
-          : (fast ? reinterpret_cast<const void*>(&append_rope_kernel<256, RW, true>)
-                  : reinterpret_cast<const void*>(&append_rope_kernel<256, RW, false>));
+  // 0: general path; 1: FAST, NeoX pairs; 2: FAST, interleaved pairs.
+  const int mode = fast ? (args.interleaved ? 2 : 1) : 0;
+  const void* const kernels[2][3] = {
+      {reinterpret_cast<const void*>(&append_rope_kernel<256, RW, 0>),
+       reinterpret_cast<const void*>(&append_rope_kernel<256, RW, 1>),
+       reinterpret_cast<const void*>(&append_rope_kernel<256, RW, 2>)},
+      {reinterpret_cast<const void*>(&append_rope_kernel<512, RW, 0>),
+       reinterpret_cast<const void*>(&append_rope_kernel<512, RW, 1>),
+       reinterpret_cast<const void*>(&append_rope_kernel<512, RW, 2>)}};
+  const void* fn = kernels[head_dim == 512 ? 1 : 0][mode];
   return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
 }
 

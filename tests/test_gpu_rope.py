@@ -280,6 +280,14 @@ def test_append_kv_rope_partial_rotation_with_full_spacing():
              freq_dim=512, theta=1e6)
 
 
+def test_append_kv_rope_longest_chunk():
+    """The largest chunk a plan accepts: 8192 new tokens of one sequence (pure prefill), pages of
+    64 keys, both pairings' fast path (R = D) and a partial one."""
+    print("rope L=8192", flush=True)
+    for rot, inter in ((256, False), (64, True)):
+        run_case(256, 2, 1, 64, [8192], 8192, rot, inter, True, True, False, seed=[89, rot])
+
+
 @pytest.mark.parametrize("L,window", [(1, 0), (24, 0), (1, 300), (64, 300)])
 def test_append_kv_rope_then_attention(L, window):
     """The decode step's order: norm + rotate + append the new tokens, then attend with the
