@@ -33,7 +33,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for required in ("decode_attn_plan", "decode_attn_global", "decode_attn_sliding",
-                     "decode_attn_stage1", "decode_attn_stage2", "decode_attn_status_str"):
+                     "decode_attn_stage1", "decode_attn_stage2", "decode_attn_append_kv",
+                     "decode_attn_rope_cache", "decode_attn_append_kv_rope",
+                     "decode_attn_status_str", "decode_attn_version"):
         assert required in names
 
 
