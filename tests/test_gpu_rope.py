@@ -405,3 +405,43 @@ def test_decode_loop_in_a_graph():
                                           w["q_weight"], w["k_weight"], None, 1e-6, 1e6, D, False)
         ref = oracle.decode_attn(q_bits[:, 0], host_k, host_v, inp.block_table, ctx, inp.scale)
         gu.compare(got, None, *ref, "graph decode step %d" % it)
+
+
+def _random_rope_cases(n=40):
+    rng = np.random.default_rng(2026)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([256, 512]))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        S = int(rng.choice([16, 32, 64, 128]))
+        L = int(rng.choice([1, 1, 2, 3, 5, 16, 40]))
+        B = int(rng.integers(1, 5))
+        ctx = [int(x) for x in rng.integers(0, 700, size=B)]
+        rot = int(rng.choice([0, 2, D // 4, D // 2, D, 2 * int(rng.integers(1, D // 2 + 1))]))
+        cases.append(dict(D=D, Hq=G * Hkv, Hkv=Hkv, S=S, L=L, ctx=ctx, rot=rot,
+                          interleaved=bool(rng.integers(0, 2)), norm_qk=bool(rng.integers(0, 2)),
+                          norm_v=bool(rng.integers(0, 2)), same_pool=bool(rng.integers(0, 4) == 0),
+                          in_place=bool(rng.integers(0, 2)), weights=bool(rng.integers(0, 3) > 0),
+                          misalign=bool(rng.integers(0, 4) == 0),
+                          max_position=(None if rng.integers(0, 3) > 0 else
+                                        int(rng.integers(1, 700))),
+                          batch=int(rng.integers(1, B + 1)), freq_dim=int(rng.choice([0, 0, D])),
+                          theta=float(rng.choice([1e4, 5e5, 1e6]))))
+    return cases
+
+
+@pytest.mark.parametrize("i,case", list(enumerate(_random_rope_cases())))
+def test_append_kv_rope_random(i, case):
+    """Seeded random combinations of every option of the step: head dim, group, KV heads, page
+    size, new tokens per sequence, ragged contexts (shorter than L included), rotated width (0,
+    2, partial, odd multiples of 2, full), pairing, norm flags, weights or none, one pool, in place,
+    4-byte-aligned tables and weights, a max_position that skips tokens, batch below the plan's,
+    frequency spacing and theta."""
+    c = case
+    print("rope random %d %s" % (i, c), flush=True)
+    run_case(c["D"], c["Hq"], c["Hkv"], c["S"], c["ctx"], c["L"], c["rot"], c["interleaved"],
+             c["norm_qk"], c["norm_v"], c["same_pool"], seed=[93, i],
+             max_position=c["max_position"], freq_dim=c["freq_dim"] if c["rot"] else 0,
+             theta=c["theta"], batch=c["batch"], in_place=c["in_place"], weights=c["weights"],
+             misalign=c["misalign"])
