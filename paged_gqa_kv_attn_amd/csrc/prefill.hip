@@ -15,8 +15,10 @@
 // and no scores cross waves:
 //
 //   - K/V tile of the step (32 keys = two 16-key entries of the tile list, each on its own page)
-//     in LDS, double-buffered; the next tile is fetched into registers during the step and
-//     written to the other buffer at its end (one barrier per step). Rows are padded by 16 bytes
+//     in LDS, double-buffered; the next tile is fetched into registers and written to the other
+//     buffer one step later (one barrier per step). At head_dim 512 the write comes first in the
+//     step and the fetch of the tile after it follows the score MFMAs, so the staging registers
+//     are free while those MFMAs read their K operands eight at a time. Rows are padded by 16 bytes
 //     and 16-byte chunks are XOR-swizzled within 64-byte groups, so the score operand reads (16
 //     keys, same column) and the P.V operand reads (16 column groups, same key) are free of
 //     bank conflicts.
@@ -45,6 +47,13 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStepKeys = 2 * kTile;  // two tile-list entries per loop step
+#ifndef DECODE_ATTN_PREFILL_KAHEAD
+#define DECODE_ATTN_PREFILL_KAHEAD 8
+#endif
+constexpr int kKAhead = DECODE_ATTN_PREFILL_KAHEAD;  // score operands read ahead of their MFMAs
+#ifndef DECODE_ATTN_PREFILL_EARLY_STORE
+#define DECODE_ATTN_PREFILL_EARLY_STORE 1  // bit 0: head_dim 512, bit 1: head_dim 256
+#endif
 
 template <int D>
 struct PShape {
@@ -72,6 +81,11 @@ template <int D, int G, bool SHARED>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
   using Sh = PShape<D>;
   constexpr int kMats = SHARED ? 1 : 2;
+  // Where the next tile is staged into LDS: at the start of the step (its registers are then free
+  // while the score MFMAs read ahead; head_dim 512, one wave per SIMD) or at its end (head_dim 256,
+  // two waves per SIMD hide each other's latency and the fetch gets the whole step to land).
+  constexpr bool kEarlyStore = (DECODE_ATTN_PREFILL_EARLY_STORE >> (D == 512 ? 0 : 1)) & 1;
+  static_assert(Sh::kQSteps % kKAhead == 0 && kKAhead % 2 == 0, "score read-ahead");
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][kMats][kStepKeys][Sh::kPitch];
 
   constexpr int kQB = kPrefillRows / G;  // queries per block
@@ -243,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
   wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
 
   // Prologue: tile of step 0 into LDS buffer 0, the tile of step 1 in flight.
-  bool ok_cur[2], ok_next[2];
+  bool ok_cur[2], ok_next[2], ok_nxt[2];
   issue_loads(t_begin, entry_pid(t_begin), entry_pid(t_begin + 1), ok_next);
   int32_t pid_next = pid_vector(t_begin + 2);
   bool full_cur = store_tile(0, t_begin, ok_next);
@@ -262,22 +276,45 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
 
   int buf = 0;
   for (int e0 = t_begin; e0 < t_end; e0 += 2) {
+    // The next step's tile (in registers since the previous step) into the other buffer, whose
+    // last readers finished before the previous step's barrier; the staging registers are then
+    // free during the score MFMAs, which read their K operands from LDS further ahead. (After the
+    // last step this stages clamped re-reads of the last entry, which are never used.)
+    bool full_nxt = false;
+    if constexpr (kEarlyStore) {
+      full_nxt = store_tile(buf ^ 1, e0 + 2, ok_next);
+      ok_nxt[0] = ok_next[0];
+      ok_nxt[1] = ok_next[1];
+    }
+
     // Scores S^T for the two entries: lane (col, grp) gets keys 4 * grp + i of entry e0 + g
     // for row my_row.
+    // The K operands are read kKAhead at a time, all issued before the MFMAs that use them.
     f32x4 sc[2];
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < Sh::kQSteps; c += 2) {
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(
-            &kv_lds[buf][0][kTile * g + col][8 * swz<D>(4 * c + grp)]);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(
-            &kv_lds[buf][0][kTile * g + col][8 * swz<D>(4 * (c + 1) + grp)]);
-        p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[c], p0, 0, 0, 0);
-        p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[c + 1], p1, 0, 0, 0);
+      for (int c0 = 0; c0 < Sh::kQSteps; c0 += kKAhead) {
+        bf16x8 kk[kKAhead];
+#pragma unroll
+        for (int c = 0; c < kKAhead; ++c)
+          kk[c] = *reinterpret_cast<const bf16x8*>(
+              &kv_lds[buf][0][kTile * g + col][8 * swz<D>(4 * (c0 + c) + grp)]);
+#pragma unroll
+        for (int c = 0; c < kKAhead; c += 2) {
+          p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[c], qop[c0 + c], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[c + 1], qop[c0 + c + 1], p1, 0, 0, 0);
+        }
       }
       sc[g] = p0 + p1;
+    }
+
+    // Fetch of the tile two steps ahead; it lands during the softmax, P.V and the barrier.
+    if constexpr (kEarlyStore) {
+      issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
+                  __builtin_amdgcn_readlane(pid_next, 1), ok_next);
+      pid_next = pid_vector(e0 + 6);
     }
 
     // Masks and online softmax of row my_row over the 32 keys.
@@ -372,15 +409,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
       }
     }
 
-    // The next step's tile (already in registers) into the other buffer, then the fetch of the
-    // step after it; one barrier publishes the buffer and retires this step's reads.
-    // (After the last step this stages clamped re-reads of the last entry, which are never used.)
-    full_cur = store_tile(buf ^ 1, e0 + 2, ok_next);
-    ok_cur[0] = ok_next[0];
-    ok_cur[1] = ok_next[1];
-    issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
-                __builtin_amdgcn_readlane(pid_next, 1), ok_next);
-    pid_next = pid_vector(e0 + 6);
+    if constexpr (!kEarlyStore) {  // stage the next tile and fetch the one after it here
+      full_nxt = store_tile(buf ^ 1, e0 + 2, ok_next);
+      ok_nxt[0] = ok_next[0];
+      ok_nxt[1] = ok_next[1];
+      issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
+                  __builtin_amdgcn_readlane(pid_next, 1), ok_next);
+      pid_next = pid_vector(e0 + 6);
+    }
+    // One barrier publishes the other buffer and retires this step's reads of this one.
+    full_cur = full_nxt;
+    ok_cur[0] = ok_nxt[0];
+    ok_cur[1] = ok_nxt[1];
     __syncthreads();
     buf ^= 1;
   }
