@@ -16,9 +16,10 @@
 //
 //   - K/V tile of the step (32 keys = two 16-key entries of the tile list, each on its own page)
 //     in LDS, double-buffered; the next tile is fetched into registers and written to the other
-//     buffer one step later (one barrier per step). At head_dim 512 the write comes first in the
-//     step and the fetch of the tile after it follows the score MFMAs, so the staging registers
-//     are free while those MFMAs read their K operands eight at a time. Rows are padded by 16 bytes
+//     buffer one step later (one barrier per step). At head_dim 512 the K half of that write
+//     comes first in the step; the score MFMAs then read their K operands eight at a time, and the
+//     V half of the write and the fetch of the tile after it follow them (a wave's LDS accesses
+//     complete in order, so the score reads wait behind the K half only). Rows are padded by 16 bytes
 //     and 16-byte chunks are XOR-swizzled within 64-byte groups, so the score operand reads (16
 //     keys, same column) and the P.V operand reads (16 column groups, same key) are free of
 //     bank conflicts.
@@ -51,6 +52,10 @@ constexpr int kStepKeys = 2 * kTile;  // two tile-list entries per loop step
 #define DECODE_ATTN_PREFILL_KAHEAD 8
 #endif
 constexpr int kKAhead = DECODE_ATTN_PREFILL_KAHEAD;  // score operands read ahead of their MFMAs
+#ifndef DECODE_ATTN_PREFILL_SPLIT_STORE
+#define DECODE_ATTN_PREFILL_SPLIT_STORE 1
+#endif
+constexpr bool kSplitStore = DECODE_ATTN_PREFILL_SPLIT_STORE;  // V half stored after the scores
 #ifndef DECODE_ATTN_PREFILL_EARLY_STORE
 #define DECODE_ATTN_PREFILL_EARLY_STORE 1  // bit 0: head_dim 512, bit 1: head_dim 256
 #endif
@@ -196,7 +201,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     const int pc = phys_tile(v < t_end ? v : t_last);
     return table_row[pc / tiles_per_page];
   };
-  auto issue_loads = [&](int e, int pid0, int pid1, bool* page_ok) {
+  // mats: bit 0 the K tile, bit 1 the V tile (no V tile when SHARED).
+  auto issue_loads = [&](int e, int pid0, int pid1, bool* page_ok, int mats) {
     const size_t base0 = entry_base(e, pid0, page_ok[0]);
     const size_t base1 = entry_base(e + 1, pid1, page_ok[1]);
     const char* k0 = reinterpret_cast<const char*>(a.k_pool + base0);
@@ -205,9 +211,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     const char* v1 = reinterpret_cast<const char*>(a.v_pool + base1);
 #pragma unroll
     for (int k = 0; k < Sh::kLoads; ++k) {
-      stk[k] = *reinterpret_cast<const u32x4*>((k < kHalf ? k0 : k1) + ld_off[k]);
+      if (mats & 1) stk[k] = *reinterpret_cast<const u32x4*>((k < kHalf ? k0 : k1) + ld_off[k]);
       if constexpr (!SHARED)
-        stv[k] = *reinterpret_cast<const u32x4*>((k < kHalf ? v0 : v1) + ld_off[k]);
+        if (mats & 2) stv[k] = *reinterpret_cast<const u32x4*>((k < kHalf ? v0 : v1) + ld_off[k]);
     }
   };
   // Key t of entry v is in the union of the block's ranges (read at all) iff its page is valid,
@@ -218,12 +224,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
   };
   // Stores the staged tile; keys outside the union are then overwritten with zeros (only entries
   // at the edges of the ranges, or of invalid pages, have any). Returns whether both are full.
-  auto store_tile = [&](int buf, int e, const bool* page_ok) -> bool {
+  auto store_tile = [&](int buf, int e, const bool* page_ok, int mats) -> bool {
 #pragma unroll
     for (int k = 0; k < Sh::kLoads; ++k) {
-      *reinterpret_cast<u32x4*>(&kv_lds[buf][0][ld_key(k)][8 * swz<D>(ld_chunk)]) = stk[k];
+      if (mats & 1) *reinterpret_cast<u32x4*>(&kv_lds[buf][0][ld_key(k)][8 * swz<D>(ld_chunk)]) = stk[k];
       if constexpr (!SHARED)
-        *reinterpret_cast<u32x4*>(&kv_lds[buf][1][ld_key(k)][8 * swz<D>(ld_chunk)]) = stv[k];
+        if (mats & 2)
+          *reinterpret_cast<u32x4*>(&kv_lds[buf][1][ld_key(k)][8 * swz<D>(ld_chunk)]) = stv[k];
     }
     const bool full = entry_full(e, page_ok[0]) && entry_full(e + 1, page_ok[1]);
     if (!full) {
@@ -235,9 +242,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
         const bool in = (v < t_end) & page_ok[k < kHalf ? 0 : 1] & (t < n) & ((t >= lo) | (t < sk));
         if (!in) {
           const u32x4 z = {0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(&kv_lds[buf][0][key][8 * swz<D>(ld_chunk)]) = z;
+          if (mats & 1) *reinterpret_cast<u32x4*>(&kv_lds[buf][0][key][8 * swz<D>(ld_chunk)]) = z;
           if constexpr (!SHARED)
-            *reinterpret_cast<u32x4*>(&kv_lds[buf][1][key][8 * swz<D>(ld_chunk)]) = z;
+            if (mats & 2) *reinterpret_cast<u32x4*>(&kv_lds[buf][1][key][8 * swz<D>(ld_chunk)]) = z;
         }
       }
     }
@@ -258,13 +265,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
 
   // Prologue: tile of step 0 into LDS buffer 0, the tile of step 1 in flight.
   bool ok_cur[2], ok_next[2], ok_nxt[2];
-  issue_loads(t_begin, entry_pid(t_begin), entry_pid(t_begin + 1), ok_next);
+  issue_loads(t_begin, entry_pid(t_begin), entry_pid(t_begin + 1), ok_next, 3);
   int32_t pid_next = pid_vector(t_begin + 2);
-  bool full_cur = store_tile(0, t_begin, ok_next);
+  bool full_cur = store_tile(0, t_begin, ok_next, 3);
   ok_cur[0] = ok_next[0];
   ok_cur[1] = ok_next[1];
   issue_loads(t_begin + 2, __builtin_amdgcn_readlane(pid_next, 0),
-              __builtin_amdgcn_readlane(pid_next, 1), ok_next);
+              __builtin_amdgcn_readlane(pid_next, 1), ok_next, 3);
   pid_next = pid_vector(t_begin + 4);
   __syncthreads();
 
@@ -282,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     // last step this stages clamped re-reads of the last entry, which are never used.)
     bool full_nxt = false;
     if constexpr (kEarlyStore) {
-      full_nxt = store_tile(buf ^ 1, e0 + 2, ok_next);
+      full_nxt = store_tile(buf ^ 1, e0 + 2, ok_next, kSplitStore ? 1 : 3);
       ok_nxt[0] = ok_next[0];
       ok_nxt[1] = ok_next[1];
     }
@@ -312,8 +319,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
 
     // Fetch of the tile two steps ahead; it lands during the softmax, P.V and the barrier.
     if constexpr (kEarlyStore) {
-      issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
-                  __builtin_amdgcn_readlane(pid_next, 1), ok_next);
+      const int pid0 = __builtin_amdgcn_readlane(pid_next, 0);
+      const int pid1 = __builtin_amdgcn_readlane(pid_next, 1);
+      if constexpr (kSplitStore) {
+        // The V half of the next tile goes to LDS only now (P.V of the next step is its first
+        // reader): the score reads above queued behind the K half's writes only, and these drain
+        // during the softmax.
+        issue_loads(e0 + 4, pid0, pid1, ok_next, 1);
+        store_tile(buf ^ 1, e0 + 2, ok_nxt, 2);
+        issue_loads(e0 + 4, pid0, pid1, ok_next, 2);
+      } else {
+        issue_loads(e0 + 4, pid0, pid1, ok_next, 3);
+      }
       pid_next = pid_vector(e0 + 6);
     }
 
@@ -410,11 +427,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     }
 
     if constexpr (!kEarlyStore) {  // stage the next tile and fetch the one after it here
-      full_nxt = store_tile(buf ^ 1, e0 + 2, ok_next);
+      full_nxt = store_tile(buf ^ 1, e0 + 2, ok_next, 3);
       ok_nxt[0] = ok_next[0];
       ok_nxt[1] = ok_next[1];
       issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
-                  __builtin_amdgcn_readlane(pid_next, 1), ok_next);
+                  __builtin_amdgcn_readlane(pid_next, 1), ok_next, 3);
       pid_next = pid_vector(e0 + 6);
     }
     // One barrier publishes the other buffer and retires this step's reads of this one.
