@@ -19,7 +19,9 @@
 //     buffer one step later (one barrier per step). At head_dim 512 the K half of that write
 //     comes first in the step; the score MFMAs then read their K operands eight at a time, and the
 //     V half of the write and the fetch of the tile after it follow them (a wave's LDS accesses
-//     complete in order, so the score reads wait behind the K half only). Rows are padded by 16 bytes
+//     complete in order, so the score reads wait behind the K half only); the V loads of that
+//     fetch are spread between the P.V column groups, so the address unit works while the MFMAs
+//     do instead of stalling the wave's issue. Rows are padded by 16 bytes
 //     and 16-byte chunks are XOR-swizzled within 64-byte groups, so the score operand reads (16
 //     keys, same column) and the P.V operand reads (16 column groups, same key) are free of
 //     bank conflicts.
@@ -56,6 +58,10 @@ constexpr int kKAhead = DECODE_ATTN_PREFILL_KAHEAD;  // score operands read ahea
 #define DECODE_ATTN_PREFILL_SPLIT_STORE 1
 #endif
 constexpr bool kSplitStore = DECODE_ATTN_PREFILL_SPLIT_STORE;  // V half stored after the scores
+#ifndef DECODE_ATTN_PREFILL_SPREAD_V
+#define DECODE_ATTN_PREFILL_SPREAD_V 1
+#endif
+constexpr bool kSpreadV = DECODE_ATTN_PREFILL_SPREAD_V;  // V loads issued between P.V column groups
 #ifndef DECODE_ATTN_PREFILL_EARLY_STORE
 #define DECODE_ATTN_PREFILL_EARLY_STORE 1  // bit 0: head_dim 512, bit 1: head_dim 256
 #endif
@@ -202,7 +208,8 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     return table_row[pc / tiles_per_page];
   };
   // mats: bit 0 the K tile, bit 1 the V tile (no V tile when SHARED).
-  auto issue_loads = [&](int e, int pid0, int pid1, bool* page_ok, int mats) {
+  auto issue_loads = [&](int e, int pid0, int pid1, bool* page_ok, int mats, int k_begin = 0,
+                         int k_end = Sh::kLoads) {
     const size_t base0 = entry_base(e, pid0, page_ok[0]);
     const size_t base1 = entry_base(e + 1, pid1, page_ok[1]);
     const char* k0 = reinterpret_cast<const char*>(a.k_pool + base0);
@@ -211,6 +218,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     const char* v1 = reinterpret_cast<const char*>(a.v_pool + base1);
 #pragma unroll
     for (int k = 0; k < Sh::kLoads; ++k) {
+      if (k < k_begin || k >= k_end) continue;
       if (mats & 1) stk[k] = *reinterpret_cast<const u32x4*>((k < kHalf ? k0 : k1) + ld_off[k]);
       if constexpr (!SHARED)
         if (mats & 2) stv[k] = *reinterpret_cast<const u32x4*>((k < kHalf ? v0 : v1) + ld_off[k]);
@@ -327,11 +335,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
         // during the softmax.
         issue_loads(e0 + 4, pid0, pid1, ok_next, 1);
         store_tile(buf ^ 1, e0 + 2, ok_nxt, 2);
-        issue_loads(e0 + 4, pid0, pid1, ok_next, 2);
+        if constexpr (!kSpreadV) issue_loads(e0 + 4, pid0, pid1, ok_next, 2);
       } else {
         issue_loads(e0 + 4, pid0, pid1, ok_next, 3);
       }
-      pid_next = pid_vector(e0 + 6);
+      if constexpr (!(kSplitStore && kSpreadV)) pid_next = pid_vector(e0 + 6);
     }
 
     // Masks and online softmax of row my_row over the 32 keys.
@@ -401,6 +409,13 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     constexpr int kV = SHARED ? 0 : 1;
 #pragma unroll
     for (int cg = 0; cg < Sh::kVGroups; ++cg) {
+      if constexpr (kEarlyStore && kSplitStore && kSpreadV) {
+        // A share of the next-but-one tile's V loads between the P.V column groups.
+        constexpr int kPer = (Sh::kLoads + Sh::kVGroups - 1) / Sh::kVGroups;
+        issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
+                    __builtin_amdgcn_readlane(pid_next, 1), ok_next, 2, cg * kPer, cg * kPer + kPer);
+        if (cg == Sh::kVGroups - 1) pid_next = pid_vector(e0 + 6);
+      }
       const int chunk = swz<D>(col * Sh::kVGroups + cg);
       u32x4 vr[8];
 #pragma unroll
