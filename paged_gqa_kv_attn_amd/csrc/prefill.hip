@@ -19,9 +19,10 @@
 //     buffer one step later (one barrier per step). At head_dim 512 the K half of that write
 //     comes first in the step; the score MFMAs then read their K operands eight at a time, and the
 //     V half of the write and the fetch of the tile after it follow them (a wave's LDS accesses
-//     complete in order, so the score reads wait behind the K half only); the V loads of that
-//     fetch are spread between the P.V column groups, so the address unit works while the MFMAs
-//     do instead of stalling the wave's issue. Rows are padded by 16 bytes
+//     complete in order, so the score reads wait behind the K half only). The loads of that fetch
+//     are spread over the step, K between the score batches and V between the P.V column groups,
+//     so the address unit works while the MFMAs do instead of stalling the wave's issue; they land
+//     directly in AGPRs, which the LDS writes read. Rows are padded by 16 bytes
 //     and 16-byte chunks are XOR-swizzled within 64-byte groups, so the score operand reads (16
 //     keys, same column) and the P.V operand reads (16 column groups, same key) are free of
 //     bank conflicts.
@@ -62,6 +63,10 @@ constexpr bool kSplitStore = DECODE_ATTN_PREFILL_SPLIT_STORE;  // V half stored 
 #define DECODE_ATTN_PREFILL_SPREAD_V 1
 #endif
 constexpr bool kSpreadV = DECODE_ATTN_PREFILL_SPREAD_V;  // V loads issued between P.V column groups
+#ifndef DECODE_ATTN_PREFILL_SPREAD_K
+#define DECODE_ATTN_PREFILL_SPREAD_K 1
+#endif
+constexpr bool kSpreadK = DECODE_ATTN_PREFILL_SPREAD_K;  // K loads issued between score batches
 #ifndef DECODE_ATTN_PREFILL_EARLY_STORE
 #define DECODE_ATTN_PREFILL_EARLY_STORE 1  // bit 0: head_dim 512, bit 1: head_dim 256
 #endif
@@ -316,6 +321,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
         for (int c = 0; c < kKAhead; ++c)
           kk[c] = *reinterpret_cast<const bf16x8*>(
               &kv_lds[buf][0][kTile * g + col][8 * swz<D>(4 * (c0 + c) + grp)]);
+        if constexpr (kEarlyStore && kSplitStore && kSpreadK) {
+          // A share of the next-but-one tile's K loads behind this batch's LDS reads.
+          constexpr int kBatches = 2 * Sh::kQSteps / kKAhead;
+          constexpr int kPer = (Sh::kLoads + kBatches - 1) / kBatches;
+          const int bi = g * (Sh::kQSteps / kKAhead) + c0 / kKAhead;
+          issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
+                      __builtin_amdgcn_readlane(pid_next, 1), ok_next, 1, bi * kPer,
+                      bi * kPer + kPer);
+        }
 #pragma unroll
         for (int c = 0; c < kKAhead; c += 2) {
           p0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[c], qop[c0 + c], p0, 0, 0, 0);
@@ -333,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
         // The V half of the next tile goes to LDS only now (P.V of the next step is its first
         // reader): the score reads above queued behind the K half's writes only, and these drain
         // during the softmax.
-        issue_loads(e0 + 4, pid0, pid1, ok_next, 1);
+        if constexpr (!kSpreadK) issue_loads(e0 + 4, pid0, pid1, ok_next, 1);
         store_tile(buf ^ 1, e0 + 2, ok_nxt, 2);
         if constexpr (!kSpreadV) issue_loads(e0 + 4, pid0, pid1, ok_next, 2);
       } else {
