@@ -423,19 +423,20 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     constexpr int kV = SHARED ? 0 : 1;
 #pragma unroll
     for (int cg = 0; cg < Sh::kVGroups; ++cg) {
-      if constexpr (kEarlyStore && kSplitStore && kSpreadV) {
-        // A share of the next-but-one tile's V loads between the P.V column groups.
-        constexpr int kPer = (Sh::kLoads + Sh::kVGroups - 1) / Sh::kVGroups;
-        issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
-                    __builtin_amdgcn_readlane(pid_next, 1), ok_next, 2, cg * kPer, cg * kPer + kPer);
-        if (cg == Sh::kVGroups - 1) pid_next = pid_vector(e0 + 6);
-      }
       const int chunk = swz<D>(col * Sh::kVGroups + cg);
       u32x4 vr[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int key = (j < 4 ? 0 : kTile) + 4 * grp + (j & 3);
         vr[j] = *reinterpret_cast<const u32x4*>(&kv_lds[buf][kV][key][8 * chunk]);
+      }
+      if constexpr (kEarlyStore && kSplitStore && kSpreadV) {
+        // A share of the next-but-one tile's V loads between the P.V column groups, behind this
+        // group's LDS reads.
+        constexpr int kPer = (Sh::kLoads + Sh::kVGroups - 1) / Sh::kVGroups;
+        issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
+                    __builtin_amdgcn_readlane(pid_next, 1), ok_next, 2, cg * kPer, cg * kPer + kPer);
+        if (cg == Sh::kVGroups - 1) pid_next = pid_vector(e0 + 6);
       }
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
