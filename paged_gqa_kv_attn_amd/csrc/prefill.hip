@@ -51,6 +51,9 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStepKeys = 2 * kTile;  // two tile-list entries per loop step
+
+// Build-time knobs of the step's order (defaults measured on MI355X; the alternatives serve A/B
+// builds).
 #ifndef DECODE_ATTN_PREFILL_KAHEAD
 #define DECODE_ATTN_PREFILL_KAHEAD 8
 #endif
@@ -97,9 +100,10 @@ template <int D, int G, bool SHARED>
 __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
   using Sh = PShape<D>;
   constexpr int kMats = SHARED ? 1 : 2;
-  // Where the next tile is staged into LDS: at the start of the step (its registers are then free
-  // while the score MFMAs read ahead; head_dim 512, one wave per SIMD) or at its end (head_dim 256,
-  // two waves per SIMD hide each other's latency and the fetch gets the whole step to land).
+  // Where the next tile is staged into LDS: around the score MFMAs (K half before them, V half
+  // after, with the fetch of the tile after it spread over the step; head_dim 512, one wave per
+  // SIMD) or at the end of the step (head_dim 256: two waves per SIMD hide each other's latency,
+  // and the fetch gets the whole step to land).
   constexpr bool kEarlyStore = (DECODE_ATTN_PREFILL_EARLY_STORE >> (D == 512 ? 0 : 1)) & 1;
   static_assert(Sh::kQSteps % kKAhead == 0 && kKAhead % 2 == 0, "score read-ahead");
   __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][kMats][kStepKeys][Sh::kPitch];
