@@ -300,10 +300,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
 
   int buf = 0;
   for (int e0 = t_begin; e0 < t_end; e0 += 2) {
-    // The next step's tile (in registers since the previous step) into the other buffer, whose
-    // last readers finished before the previous step's barrier; the staging registers are then
-    // free during the score MFMAs, which read their K operands from LDS further ahead. (After the
-    // last step this stages clamped re-reads of the last entry, which are never used.)
+    // The K half of the next step's tile (in registers since the previous step) into the other
+    // buffer, whose last readers finished before the previous step's barrier. Its registers then
+    // take the fetch of the tile after it, issued between the score batches. (After the last step
+    // this stages clamped re-reads of the last entry, which are never used.)
     bool full_nxt = false;
     if constexpr (kEarlyStore) {
       full_nxt = store_tile(buf ^ 1, e0 + 2, ok_next, kSplitStore ? 1 : 3);
