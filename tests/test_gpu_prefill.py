@@ -84,6 +84,24 @@ def test_prefill_values_equal_keys():
     gu.compare(out, lse, *gu.reference(inp), "prefill k=v")
 
 
+@pytest.mark.parametrize("window,sink", [(0, 0), (300, 4)])
+def test_prefill_values_equal_keys_forced_splits(window, sink):
+    """K = V at head_dim 512 (one pool for both, each tile staged once) with split counts that
+    leave 1 to 3 tile-list entries per split, so the last step of a split stages clamped re-reads,
+    on lengths that end inside a page; a windowed variant with sinks."""
+    print("prefill k=v forced splits W=%d sink=%d" % (window, sink), flush=True)
+    ctx = [197, 250, 83]
+    inp = make_layer_inputs(ctx, 16, 2, 512, page_size=16, window=window, sink=sink,
+                            seed=[77, window, sink], q_mult=1.5, q_len=80)
+    inp.v_pool = inp.k_pool
+    t = gu.upload(inp)
+    t["v"] = t["k"]
+    ref = gu.reference(inp)
+    for splits in (0, 7, 11, 16):
+        out, lse = gu.run(inp, dev_bufs=t, values_are_keys=True, force_splits=splits)
+        gu.compare(out, lse, *ref, "prefill k=v W%d sink%d ns%d" % (window, sink, splits))
+
+
 def test_prefill_longest_chunk():
     """The largest chunk a plan accepts: 8192 queries, pure prefill of an 8192-token prompt, with
     pages of 64 keys."""
