@@ -636,3 +636,54 @@ def test_append_rejects_positions_outside_the_table():
     with pytest.raises(ValueError):
         oracle.append_kv(np.zeros((1, 1, 16), np.uint16), np.zeros((1, 1, 16), np.uint16),
                          inp.k_pool, inp.v_pool, inp.block_table, ctx)
+
+
+def _row_code(b, i, g, D, sign=1.0):
+    """A row whose every element names (sequence b, new token i, KV head g): 16 b + 4 i + g, plus
+    d % 4 quarters so a row read at a shifted column also fails. Exact in bf16 (at most 8
+    significant bits)."""
+    return bf([sign * (16 * b + 4 * i + g + 0.25 * (d % 4)) for d in range(D)])
+
+
+# Slots of the L = 3 newest tokens, placed by hand from the block table below (page size 4):
+#   b0: ctx 6  -> positions 3, 4, 5:   column 0 (page 5) slot 3, column 1 (page 2) slots 0 and 1
+#   b1: ctx 2  -> positions -1, 0, 1:  token 0 skipped, column 0 (page 1) slots 0 and 1
+#   b2: ctx 12 -> positions 9, 10, 11: column 2 (page 4) slots 1, 2, 3
+_APPEND_TABLE = [[5, 2, 7], [1, 6, -1], [3, 0, 4]]
+_APPEND_CTX = [6, 2, 12]
+_APPEND_SLOTS = {  # (b, i) -> (page, slot)
+    (0, 0): (5, 3), (0, 1): (2, 0), (0, 2): (2, 1),
+    (1, 1): (1, 0), (1, 2): (1, 1),
+    (2, 0): (4, 1), (2, 1): (4, 2), (2, 2): (4, 3),
+}
+
+
+@pytest.mark.parametrize("one_pool", [False, True])
+def test_append_several_tokens_lands_in_hand_placed_slots(one_pool):
+    """L = 3 new tokens per sequence, across a page boundary, with a position below 0 skipped:
+    every (b, i, g) row lands in the slot worked out by hand above and no other slot changes. A
+    reversed token order, a swapped b / i stride or a page / slot mix-up moves some row."""
+    B, L, Hkv, D, S, P = 3, 3, 2, 8, 4, 8
+    k_new = np.stack([np.stack([np.stack([_row_code(b, i, g, D) for g in range(Hkv)])
+                                for i in range(L)]) for b in range(B)])
+    v_new = np.stack([np.stack([np.stack([_row_code(b, i, g, D, -1.0) for g in range(Hkv)])
+                                for i in range(L)]) for b in range(B)])
+    sentinel = bf([-3.5])[0]
+    k_pool = np.full((P, Hkv, S, D), sentinel, np.uint16)
+    v_pool = k_pool if one_pool else np.full((P, Hkv, S, D), sentinel, np.uint16)
+    table = np.array(_APPEND_TABLE, np.int32)
+    ctx = np.array(_APPEND_CTX, np.int32)
+    oracle.append_kv(k_new, None if one_pool else v_new, k_pool, v_pool, table, ctx)
+
+    expect_k = np.full((P, Hkv, S, D), sentinel, np.uint16)
+    expect_v = np.full((P, Hkv, S, D), sentinel, np.uint16)
+    for (b, i), (page, slot) in _APPEND_SLOTS.items():
+        for g in range(Hkv):
+            expect_k[page, g, slot] = _row_code(b, i, g, D)
+            expect_v[page, g, slot] = _row_code(b, i, g, D, -1.0)
+    np.testing.assert_array_equal(k_pool, expect_k)
+    if not one_pool:
+        np.testing.assert_array_equal(v_pool, expect_v)
+    # The skipped token (b1, i0) was written nowhere.
+    for g in range(Hkv):
+        assert not (k_pool == _row_code(1, 0, g, D)).all(axis=-1).any()
