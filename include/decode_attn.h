@@ -54,7 +54,8 @@
  *     ctx_lens     [B]                    int32
  *     out          [B, L, Hq, D]          fp32
  *     lse_out      [B, L, Hq]             fp32   (optional, may be NULL)
- *     workspace    workspace_bytes bytes  stage-1 partials, see decode_attn_stage1
+ *     workspace    stage-1 partials (see decode_attn_stage1): plan->workspace_bytes bytes for the
+ *                  stage calls, plan->layer_workspace_bytes for the layer calls
  *
  * Ownership and threading. Every buffer is owned by the caller; the library never allocates or
  * frees device memory and keeps no mutable global state (a per-device CU count is cached). Calls
@@ -84,7 +85,7 @@ typedef enum {
   DECODE_ATTN_ERR_NULL = 1,        /* a required pointer is NULL */
   DECODE_ATTN_ERR_SHAPE = 2,       /* inconsistent sizes or values (Hq % Hkv != 0, batch > plan) */
   DECODE_ATTN_ERR_UNSUPPORTED = 3, /* head_dim, group size or page size with no compiled kernel */
-  DECODE_ATTN_ERR_WORKSPACE = 4,   /* workspace smaller than plan->workspace_bytes */
+  DECODE_ATTN_ERR_WORKSPACE = 4,   /* workspace smaller than the call needs (see the plan) */
   DECODE_ATTN_ERR_PLAN = 5,        /* plan not made by decode_attn_plan, or for the other layer kind */
   DECODE_ATTN_ERR_HIP = 6,         /* the HIP runtime reported an error (launch or device query) */
   DECODE_ATTN_ERR_ALIGN = 7        /* q, pools, out or workspace not 16-byte aligned */
@@ -126,10 +127,15 @@ typedef struct {
   int32_t chunk_tokens;        /* tokens per chunk at max_ctx_len (16-token tiles, informational) */
   int32_t group_size;          /* G = Hq / Hkv */
   int32_t kind;                /* 1 = global (window == 0), 2 = sliding (window > 0) */
-  uint64_t workspace_bytes;    /* bytes of workspace every call with this plan needs */
+  uint64_t workspace_bytes;    /* bytes of workspace decode_attn_stage1 / _stage2 need */
   uint64_t partial_lse_offset; /* byte offset of the LSE plane inside the workspace */
   uint32_t magic;              /* set by decode_attn_plan; checked by every entry point */
-  int32_t reserved[7];
+  int32_t reserved0;
+  uint64_t layer_workspace_bytes; /* bytes of workspace decode_attn_global / _sliding need:
+                                     workspace_bytes, or with num_splits == 1 only the
+                                     256-byte-rounded [B, L, Hq] fp32 lse plane (stage 1 then
+                                     writes out in place and its lse there when lse_out is NULL) */
+  int32_t reserved[4];
 } decode_attn_plan_t;
 
 /*
@@ -152,7 +158,7 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
  * decode_attn_global — attention of a global layer (plan->problem.window == 0): stage 1 then
  * stage 2 on `stream` (stage 1 alone, writing out and lse_out, when plan->num_splits == 1). `batch` (0 <= batch <= plan->problem.batch) sequences are computed; batch 0
  * returns DECODE_ATTN_OK without launching. `scale` multiplies q.k (1/sqrt(D) for Gemma-style
- * layers). lse_out may be NULL. workspace must hold plan->workspace_bytes. A plan made with
+ * layers). lse_out may be NULL. workspace must hold plan->layer_workspace_bytes. A plan made with
  * values_are_keys = 1 requires v_pool == k_pool (else DECODE_ATTN_ERR_SHAPE); the same pool passed
  * twice under a plan without it is computed correctly, with the other split count.
  */
@@ -284,8 +290,8 @@ const char* decode_attn_status_str(int status);
 /* Library version, major * 10000 + minor * 100 + patch. The minor number changes with the layout
  * of decode_attn_problem / decode_attn_plan_t (0.2: sink and q_len fields); 0.2.1: q_len up to
  * 8192, one-split calls without stage 2; 0.2.2: decode_attn_rope_cache and
- * decode_attn_append_kv_rope. */
-#define DECODE_ATTN_VERSION 202
+ * decode_attn_append_kv_rope; 0.3.0: layer_workspace_bytes in the plan. */
+#define DECODE_ATTN_VERSION 300
 int decode_attn_version(void);
 
 #ifdef __cplusplus

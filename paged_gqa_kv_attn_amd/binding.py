@@ -56,7 +56,9 @@ class Plan(ctypes.Structure):
         ("workspace_bytes", ctypes.c_uint64),
         ("partial_lse_offset", ctypes.c_uint64),
         ("magic", ctypes.c_uint32),
-        ("reserved", ctypes.c_int32 * 7),
+        ("reserved0", ctypes.c_int32),
+        ("layer_workspace_bytes", ctypes.c_uint64),
+        ("reserved", ctypes.c_int32 * 4),
     ]
 
     def __repr__(self):
@@ -74,7 +76,7 @@ def library_path() -> str:
 
 
 # decode_attn_version() of the library whose struct layouts Problem and Plan mirror.
-ABI_VERSION = 202
+ABI_VERSION = 300
 
 
 def load_library():

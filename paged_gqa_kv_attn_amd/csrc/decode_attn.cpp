@@ -56,6 +56,15 @@ void workspace_layout(const decode_attn_problem& p, int num_splits, uint64_t* ls
   *total = align_up(*lse_offset + rows * 4u, 256);
 }
 
+// Workspace of a layer call (decode_attn_global / _sliding): the stage workspace, or with one
+// split only the lse plane [B, L, Hq] (stage 1 writes out in place, and its lse into the
+// workspace at offset 0 when the caller passes no lse_out).
+uint64_t layer_workspace(const decode_attn_problem& p, int num_splits, uint64_t stage_total) {
+  if (num_splits != 1) return stage_total;
+  const uint64_t rows = (uint64_t)p.batch * (uint64_t)q_len_of(p) * (uint64_t)p.num_q_heads;
+  return align_up(rows * 4u, 256);
+}
+
 bool aligned(const void* ptr, uintptr_t a) { return ((uintptr_t)ptr % a) == 0; }
 
 // Checks a plan made by decode_attn_plan and not altered since.
@@ -76,15 +85,17 @@ int check_plan(const decode_attn_plan_t* plan) {
     return DECODE_ATTN_ERR_PLAN;
   uint64_t lse_off = 0, total = 0;
   workspace_layout(p, plan->num_splits, &lse_off, &total);
-  if (plan->workspace_bytes != total || plan->partial_lse_offset != lse_off)
+  if (plan->workspace_bytes != total || plan->partial_lse_offset != lse_off ||
+      plan->layer_workspace_bytes != layer_workspace(p, plan->num_splits, total))
     return DECODE_ATTN_ERR_PLAN;
   return DECODE_ATTN_OK;
 }
 
+// needed: the workspace bytes the call requires (the stage or the layer figure of the plan).
 int check_stage1_args(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
                       const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens,
                       int32_t batch, float scale, const void* workspace,
-                      uint64_t workspace_bytes) {
+                      uint64_t workspace_bytes, uint64_t needed) {
   if (batch < 0 || batch > plan->problem.batch) return DECODE_ATTN_ERR_SHAPE;
   if (!std::isfinite(scale)) return DECODE_ATTN_ERR_SHAPE;
   if (batch == 0) return DECODE_ATTN_OK;
@@ -94,18 +105,19 @@ int check_stage1_args(const decode_attn_plan_t* plan, const void* q, const void*
       !aligned(block_table, 4) || !aligned(ctx_lens, 4))
     return DECODE_ATTN_ERR_ALIGN;
   if (plan->problem.values_are_keys && k_pool != v_pool) return DECODE_ATTN_ERR_SHAPE;
-  if (workspace_bytes < plan->workspace_bytes) return DECODE_ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < needed) return DECODE_ATTN_ERR_WORKSPACE;
   return DECODE_ATTN_OK;
 }
 
 int check_stage2_args(const decode_attn_plan_t* plan, int32_t batch, const void* workspace,
-                      uint64_t workspace_bytes, const float* out, const float* lse_out) {
+                      uint64_t workspace_bytes, const float* out, const float* lse_out,
+                      uint64_t needed) {
   if (batch < 0 || batch > plan->problem.batch) return DECODE_ATTN_ERR_SHAPE;
   if (batch == 0) return DECODE_ATTN_OK;
   if (!workspace || !out) return DECODE_ATTN_ERR_NULL;
   if (!aligned(workspace, 16) || !aligned(out, 16) || (lse_out && !aligned(lse_out, 4)))
     return DECODE_ATTN_ERR_ALIGN;
-  if (workspace_bytes < plan->workspace_bytes) return DECODE_ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < needed) return DECODE_ATTN_ERR_WORKSPACE;
   return DECODE_ATTN_OK;
 }
 
@@ -165,19 +177,21 @@ int attend(const decode_attn_plan_t* plan, int expected_kind, const void* q, con
   if (rc != DECODE_ATTN_OK) return rc;
   if (plan->kind != expected_kind) return DECODE_ATTN_ERR_PLAN;
   rc = check_stage1_args(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, workspace,
-                         workspace_bytes);
+                         workspace_bytes, plan->layer_workspace_bytes);
   if (rc != DECODE_ATTN_OK) return rc;
-  rc = check_stage2_args(plan, batch, workspace, workspace_bytes, out, lse_out);
+  rc = check_stage2_args(plan, batch, workspace, workspace_bytes, out, lse_out,
+                         plan->layer_workspace_bytes);
   if (rc != DECODE_ATTN_OK || batch == 0) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->partial_lse_offset);
   if (plan->num_splits == 1) {
     // One chunk per row: its normalised output and log-sum-exp already are the result, and the
     // partial planes [B, L, Hq, 1, D] / [B, L, Hq, 1] have the layout of out / lse_out, so stage 1
-    // writes them in place and the merge is skipped.
+    // writes them in place and the merge is skipped. Without lse_out the lse goes to the
+    // workspace, which then holds only that plane.
     return run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, out,
-                      lse_out != nullptr ? lse_out : lse_ws, s);
+                      lse_out != nullptr ? lse_out : static_cast<float*>(workspace), s);
   }
+  float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan->partial_lse_offset);
   rc = run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale,
                   static_cast<float*>(workspace), lse_ws, s);
   if (rc != DECODE_ATTN_OK) return rc;
@@ -256,6 +270,7 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   out.group_size = G;
   out.kind = p.window > 0 ? 2 : 1;
   workspace_layout(p, out.num_splits, &out.partial_lse_offset, &out.workspace_bytes);
+  out.layer_workspace_bytes = layer_workspace(p, out.num_splits, out.workspace_bytes);
   out.magic = kPlanMagic;
   *plan = out;
   return DECODE_ATTN_OK;
@@ -288,7 +303,7 @@ int decode_attn_stage1(const decode_attn_plan_t* plan, const void* q, const void
   int rc = check_plan(plan);
   if (rc != DECODE_ATTN_OK) return rc;
   rc = check_stage1_args(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale, workspace,
-                         workspace_bytes);
+                         workspace_bytes, plan->workspace_bytes);
   if (rc != DECODE_ATTN_OK || batch == 0) return rc;
   return run_stage1(plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale,
                     static_cast<float*>(workspace),
@@ -301,7 +316,8 @@ int decode_attn_stage2(const decode_attn_plan_t* plan, int32_t batch, const void
                        uint64_t workspace_bytes, float* out, float* lse_out, void* stream) {
   int rc = check_plan(plan);
   if (rc != DECODE_ATTN_OK) return rc;
-  rc = check_stage2_args(plan, batch, workspace, workspace_bytes, out, lse_out);
+  rc = check_stage2_args(plan, batch, workspace, workspace_bytes, out, lse_out,
+                         plan->workspace_bytes);
   if (rc != DECODE_ATTN_OK || batch == 0) return rc;
   return run_stage2(plan, batch, workspace, out, lse_out, static_cast<hipStream_t>(stream));
 }

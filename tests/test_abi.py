@@ -45,10 +45,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_plan_struct_layout_matches_header():
-    # 15 int32 problem fields, 4 int32, 2 uint64, uint32 magic, 7 int32 reserved (+ padding)
+    # 15 int32 problem fields, 4 int32, 2 uint64, uint32 magic, int32, uint64, 4 int32 reserved
     assert ctypes.sizeof(binding.Problem) == 60
     assert binding.Plan.workspace_bytes.offset == 80
     assert binding.Plan.magic.offset == 96
+    assert binding.Plan.layer_workspace_bytes.offset == 104
     assert ctypes.sizeof(binding.Plan) == 128
 
 
@@ -99,6 +100,8 @@ def test_plan_split_counts(kw, splits):
     off, total = expected_workspace(p.problem.batch, p.problem.num_q_heads, splits,
                                     p.problem.head_dim, p.problem.q_len)
     assert p.partial_lse_offset == off and p.workspace_bytes == total
+    rows = p.problem.batch * max(1, p.problem.q_len) * p.problem.num_q_heads
+    assert p.layer_workspace_bytes == (total if splits > 1 else -(-rows * 4 // 256) * 256)
     assert p.magic == binding.PLAN_MAGIC
 
 
@@ -190,6 +193,21 @@ def test_entry_validation_before_launch(lib):
     # batch 0 is a no-op: no pointer is needed and nothing is launched
     assert call_global(lib, p, q=None, k=None, v=None, bt=None, ctx=None, out=None, ws=None,
                        wsb=0, batch=0) == OK
+
+
+def test_one_split_layer_call_needs_only_the_lse_plane(lib):
+    """A one-split plan (a prefill chunk) asks the layer calls for the [B, L, Hq] lse plane only,
+    and the stage calls still for the whole partial buffer."""
+    p = plan(batch=1, q_len=8192, max_pages_per_seq=600, max_ctx_len=9000)
+    assert p.num_splits == 1
+    rows = 1 * 8192 * 16
+    assert p.layer_workspace_bytes == rows * 4 < p.workspace_bytes // 100
+    assert call_global(lib, p, wsb=p.layer_workspace_bytes - 1) == ERR_WORKSPACE
+    assert lib.decode_attn_stage1(ctypes.byref(p), A, A, A, A, A, 1, 0.1, A,
+                                  p.layer_workspace_bytes, None) == ERR_WORKSPACE
+    bad = binding.Plan.from_buffer_copy(p)
+    bad.layer_workspace_bytes -= 256
+    assert call_global(lib, bad) == ERR_PLAN
 
 
 def test_plan_tampering_and_kind(lib):
@@ -294,7 +312,7 @@ def test_status_strings(lib):
     for code in range(8):
         assert binding.decode_attn_status_str(code).startswith(binding.STATUS_NAMES[code])
     assert "unknown" in binding.decode_attn_status_str(99)
-    assert binding.decode_attn_version() == binding.ABI_VERSION == 202
+    assert binding.decode_attn_version() == binding.ABI_VERSION == 300
 
 
 def test_binding_rejects_tensors_smaller_than_the_plan():

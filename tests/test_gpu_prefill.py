@@ -46,22 +46,26 @@ def test_prefill_one_split_chunks(L):
 
 
 def test_prefill_one_split_without_lse_output():
-    """With one split and lse_out NULL the chunk's lse goes to the workspace; out is unchanged."""
+    """With one split and lse_out NULL the chunk's lse goes to the workspace, which then needs only
+    the [B, L, Hq] lse plane (plan.layer_workspace_bytes); out is unchanged."""
     import torch
     import paged_gqa_kv_attn_amd as pda
     gu.ensure_library()
     inp = make_layer_inputs([600, 813], 16, 2, 512, page_size=16, seed=73, q_len=600)
     plan = gu.make_plan(inp)
     assert plan.num_splits == 1
-    t = gu.upload(inp)
     d = inp.dims
+    rows = d["B"] * inp.q_len * d["Hq"]
+    assert plan.layer_workspace_bytes == -(-rows * 4 // 256) * 256 < plan.workspace_bytes
+    t = gu.upload(inp)
     out = torch.full((d["B"], inp.q_len, d["Hq"], d["D"]), float("nan"), device=gu.device())
-    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=gu.device())
+    ws = torch.full((plan.layer_workspace_bytes // 4,), float("nan"), device=gu.device())
     pda.decode_attn_global(plan, t["q"], t["k"], t["v"], t["bt"], t["ctx"], d["B"], inp.scale,
                            out, None, ws)
     torch.cuda.synchronize()
     ref_out, ref_lse = gu.reference(inp)
-    gu.compare(out.cpu().numpy(), None, ref_out, ref_lse, "prefill no lse")
+    lse_ws = ws[:rows].view(d["B"], inp.q_len, d["Hq"]).cpu().numpy()
+    gu.compare(out.cpu().numpy(), lse_ws, ref_out, ref_lse, "prefill no lse")
 
 
 @pytest.mark.parametrize("window,sink", [(128, 0), (128, 4), (1024, 16)])
