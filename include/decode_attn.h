@@ -284,6 +284,31 @@ int decode_attn_append_kv_rope(const decode_attn_plan_t* plan, const void* q, vo
                                const float* k_norm_weight, const float* v_norm_weight, float eps,
                                void* stream);
 
+/* Size of the device array behind decode_attn_layer_noalloc (64 MiB per device). */
+#define DECODE_ATTN_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/*
+ * decode_attn_layer_noalloc — for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the layer call of
+ * decode_attn_global (window == 0) or decode_attn_sliding (window == plan->problem.window > 0)
+ * with the same arguments minus the workspace. The stage-1 partials go to a static device array
+ * of the library, DECODE_ATTN_NOALLOC_SCRATCH_BYTES long, that every device running the library
+ * holds until the process ends; no call allocates or frees anything. Results are those of the
+ * layer call with a caller workspace (the same kernels).
+ * Limit: plans whose layer_workspace_bytes exceed DECODE_ATTN_NOALLOC_SCRATCH_BYTES are rejected
+ * with DECODE_ATTN_ERR_WORKSPACE before anything else is touched (single-token decode needs
+ * B * Hq * num_splits * (D + 1) * 4 bytes: 4.2 MB for 4 x 32K or 1 x 128K at 16 heads, D 512).
+ * Sharing: all calls on one device use that device's one array, so calls that may overlap on
+ * a device (other streams, other host threads) race and must be ordered by the caller; each call
+ * writes every partial it reads, so nothing carries over from the previous call.
+ * The first call on a device looks up the array's address there (hipGetSymbolAddress); make it
+ * outside graph capture. Errors: those of decode_attn_global / _sliding.
+ */
+int decode_attn_layer_noalloc(const decode_attn_plan_t* plan, const void* q, const void* k_pool,
+                              const void* v_pool, const int32_t* block_table,
+                              const int32_t* ctx_lens, int32_t batch, int32_t window, float scale,
+                              float* out, float* lse_out, void* stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* decode_attn_status_str(int status);
 

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     decode_attn_append_kv,
     decode_attn_append_kv_rope,
     decode_attn_global,
+    decode_attn_layer_noalloc,
     decode_attn_plan,
     decode_attn_rope_cache,
     decode_attn_sliding,

@@ -106,9 +106,12 @@ def load_library():
     lib.decode_attn_rope_cache.argtypes = [vp, i32, i32, i32, ctypes.c_double, vp]
     lib.decode_attn_append_kv_rope.argtypes = [pplan, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i32,
                                                i32, i32, i32, vp, vp, vp, f32, vp]
+    lib.decode_attn_layer_noalloc.argtypes = [pplan, vp, vp, vp, vp, vp, i32, i32, f32, vp, vp,
+                                              vp]
     for fn in ("decode_attn_plan", "decode_attn_global", "decode_attn_sliding",
                "decode_attn_stage1", "decode_attn_stage2", "decode_attn_append_kv",
-               "decode_attn_rope_cache", "decode_attn_append_kv_rope"):
+               "decode_attn_rope_cache", "decode_attn_append_kv_rope",
+               "decode_attn_layer_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.decode_attn_status_str.argtypes = [ctypes.c_int]
     lib.decode_attn_status_str.restype = ctypes.c_char_p
@@ -269,6 +272,26 @@ def decode_attn_sliding(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, ba
         _dev_ptr(ctx_lens, "ctx_lens", _i32(), dev), int(batch), int(window), float(scale),
         _dev_ptr(out, "out", _f32(), dev), _dev_ptr(lse_out, "lse_out", _f32(), dev), ws, wsb,
         _stream_handle(stream)), "decode_attn_sliding")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DECODE_ATTN_NOALLOC_SCRATCH_BYTES
+
+
+def decode_attn_layer_noalloc(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, batch, window,
+                              scale, out, lse_out=None, stream=None) -> None:
+    """The layer call (global for window 0, else sliding) with the partials in the library's
+    static device array instead of a caller workspace: nothing is allocated. Calls that may
+    overlap on one device share that array and must be ordered by the caller."""
+    lib = load_library()
+    dev = _current_device()
+    _check_sizes(plan, batch, q, k_pool, v_pool, block_table, ctx_lens, out, lse_out)
+    _check(lib.decode_attn_layer_noalloc(
+        ctypes.byref(plan), _dev_ptr(q, "q", _bf16(), dev),
+        _dev_ptr(k_pool, "k_pool", _bf16(), dev), _dev_ptr(v_pool, "v_pool", _bf16(), dev),
+        _dev_ptr(block_table, "block_table", _i32(), dev),
+        _dev_ptr(ctx_lens, "ctx_lens", _i32(), dev), int(batch), int(window), float(scale),
+        _dev_ptr(out, "out", _f32(), dev), _dev_ptr(lse_out, "lse_out", _f32(), dev),
+        _stream_handle(stream)), "decode_attn_layer_noalloc")
 
 
 def decode_attn_stage1(plan: Plan, q, k_pool, v_pool, block_table, ctx_lens, batch, scale,

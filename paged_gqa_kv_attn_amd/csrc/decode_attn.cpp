@@ -169,6 +169,8 @@ int run_stage2(const decode_attn_plan_t* plan, int32_t batch, const void* worksp
   return DECODE_ATTN_OK;
 }
 
+}  // namespace
+
 int attend(const decode_attn_plan_t* plan, int expected_kind, const void* q, const void* k_pool,
            const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens, int32_t batch,
            float scale, float* out, float* lse_out, void* workspace, uint64_t workspace_bytes,
@@ -198,7 +200,6 @@ int attend(const decode_attn_plan_t* plan, int expected_kind, const void* q, con
   return run_stage2(plan, batch, workspace, out, lse_out, s);
 }
 
-}  // namespace
 }  // namespace decode_attn
 
 using namespace decode_attn;

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
+#include "decode_attn.h"
+
 namespace decode_attn {
 
 constexpr uint32_t kPlanMagic = 0x44415431u;  // "DAT1"
@@ -105,6 +107,14 @@ hipError_t launch_rope_cache(float* cos_sin, int max_position, int rotary_dim, i
                              double theta, hipStream_t stream);
 hipError_t launch_append_rope(const AppendRopeArgs& args, int head_dim, int batch,
                               hipStream_t stream);
+
+// The layer call behind decode_attn_global (expected_kind 1) and decode_attn_sliding (2): checks
+// the plan and the arguments against plan->layer_workspace_bytes, then launches stage 1 (and
+// stage 2 when the plan has more than one split). decode_attn.cpp.
+int attend(const decode_attn_plan_t* plan, int expected_kind, const void* q, const void* k_pool,
+           const void* v_pool, const int32_t* block_table, const int32_t* ctx_lens, int32_t batch,
+           float scale, float* out, float* lse_out, void* workspace, uint64_t workspace_bytes,
+           void* stream);
 
 // True when a stage-1 kernel is compiled for (head_dim, group_size).
 bool stage1_supported(int head_dim, int group_size);

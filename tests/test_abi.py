@@ -210,6 +210,26 @@ def test_one_split_layer_call_needs_only_the_lse_plane(lib):
     assert call_global(lib, bad) == ERR_PLAN
 
 
+def test_noalloc_rejects_before_touching_the_device(lib):
+    """The allocation-free layer call checks the plan, the window and the scratch limit before it
+    looks up its device array."""
+    f = lib.decode_attn_layer_noalloc
+    args = (A, A, A, A, A, 1)
+    big = plan(force_splits=1024)  # 4 x 16 heads x 1024 splits x 513 x 4 B > 64 MiB
+    assert big.layer_workspace_bytes > binding.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), *args, 0, 0.1, A, None, None) == ERR_WORKSPACE
+    p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600)
+    assert f(None, *args, 0, 0.1, A, None, None) == ERR_NULL
+    assert f(ctypes.byref(p), *args, 1024, 0.1, A, None, None) == ERR_SHAPE  # global plan
+    bad = binding.Plan.from_buffer_copy(p)
+    bad.magic = 0
+    assert f(ctypes.byref(bad), *args, 0, 0.1, A, None, None) == ERR_PLAN
+    assert f(ctypes.byref(p), A, A, A, A, A, 0, 0, 0.1, A, None, None) == OK  # batch 0: no-op
+    s = plan(batch=2, num_kv_heads=8, head_dim=256, window=1024, max_pages_per_seq=100,
+             max_ctx_len=1600)
+    assert f(ctypes.byref(s), *args, 512, 0.1, A, None, None) == ERR_SHAPE
+
+
 def test_plan_tampering_and_kind(lib):
     p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600)
     bad = binding.Plan.from_buffer_copy(p)
