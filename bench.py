@@ -73,6 +73,63 @@ def load_traffic(workload: str, num_splits: int):
         return None
 
 
+def load_trace_mean_us(workload: str):
+    """Mean duration (us) of the global stage-1 kernel in the committed rocprofv3 kernel-trace
+    summary of this workload, if it was taken with the same device code as now (else None)."""
+    import re
+    path = os.path.join(ROOT, "profiles", "stage1_global_%s_kernel_trace.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"^kernel_code_sha256_16:\s*(\S+)", text, re.M)
+    m = re.search(r"^(?:dominant kernel|global stage 1) stage1_kernel.*mean ([0-9.]+) us", text,
+                  re.M)
+    if h is None or m is None or h.group(1) != kernel_code_hash():
+        return None
+    return float(m.group(1))
+
+
+def provenance() -> dict:
+    """Where the numbers come from: the source revision the library was built from, the ROCm and
+    torch versions, the device."""
+    import subprocess
+    info = {}
+    try:
+        sha = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10)
+        if sha.returncode == 0:
+            dirty = subprocess.run(["git", "-C", ROOT, "status", "--porcelain",
+                                    "--untracked-files=no"], capture_output=True, text=True,
+                                   timeout=10)
+            info["git_sha"] = sha.stdout.strip()
+            info["git_dirty"] = bool(dirty.stdout.strip())
+            info["git_source"] = "working tree"
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if "git_sha" not in info:
+        # No repository here (a copied tree): the revision recorded when the library was built.
+        try:
+            with open(os.path.join(ROOT, "paged_gqa_kv_attn_amd", "_build_info.json")) as f:
+                b = json.load(f)
+            info.update(git_sha=b.get("git_sha"), git_dirty=b.get("git_dirty"),
+                        git_source="recorded at library build")
+        except (OSError, ValueError):
+            info.update(git_sha=None, git_dirty=None, git_source="unavailable")
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm_version"] = f.read().strip()
+    except OSError:
+        info["rocm_version"] = None
+    import torch
+    info["torch_version"] = torch.__version__
+    info["torch_hip_version"] = getattr(torch.version, "hip", None)
+    if torch.cuda.is_available():
+        props = torch.cuda.get_device_properties(0)
+        info["device"] = "%s (%s), %d CUs" % (props.name, getattr(props, "gcnArchName", "?"),
+                                             props.multi_processor_count)
+    return info
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -101,6 +158,10 @@ def main() -> int:
                     help="skip the graph-replay diagnostic after the timed region")
     ap.add_argument("--sink", type=int, default=0,
                     help="sink keys the sliding layer also attends (StreamingLLM-style view)")
+    ap.add_argument("--range", default="very_long_b2,very_long_b1",
+                    help="further workloads whose global layer is timed after the step (cold and "
+                         "hot call medians, back-to-back stage-1 launches): by default the 2 x 64K "
+                         "and 1 x 128K ends of the 32K-128K range; '' for none")
     args = ap.parse_args()
 
     if args.append and args.rope:
@@ -333,6 +394,32 @@ def main() -> int:
         graph_us = 1e3 * ga.elapsed_time(gb) / K
         del graphs
 
+    # The dominant kernel on its own: back-to-back stage-1 launches of the global layer (rotating
+    # pool copies) between one event pair on the launch stream; the average per launch includes
+    # the dispatch gap between kernels but not an event pair's own overhead per launch.
+    def stage1_only(L, r):
+        p = L["plan"]
+        if p.num_splits == 1:
+            pda.decode_attn_global(p, L["q"], L["k"][r], L["v"][r], L["bt"], L["ctx"],
+                                   p.problem.batch, L["inp"].scale, L["out"], L["lse"], L["ws"])
+        else:
+            pda.decode_attn_stage1(p, L["q"], L["k"][r], L["v"][r], L["bt"], L["ctx"],
+                                   p.problem.batch, L["inp"].scale, L["ws"])
+
+    def back_to_back_us(L, n, fn):
+        for i in range(3):
+            fn(L, i % len(L["k"]))
+        ba, bb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ba.record(stream)
+        for i in range(n):
+            fn(L, i % len(L["k"]))
+        bb.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * ba.elapsed_time(bb) / n
+
+    s1_b2b_us = back_to_back_us(dominant, K, stage1_only)
+
     # Per-layer breakdown, after (outside) the timed region: events around each layer call.
     # Cold: before every call a 512 MB buffer is written (outside the event pair), which evicts
     # the L2s and the MALL, so the call reads its K/V from HBM whatever the workload's size.
@@ -384,6 +471,81 @@ def main() -> int:
                                      append_bytes=L["append_bytes"],
                                      append_GB_per_s=round(L["append_bytes"] /
                                                            (L["append_us"] * 1e-6) / 1e9, 1))
+    # The other ends of the 32K-128K range: each workload's global layer on its own (inputs made
+    # here, two pool copies rotated), timed like the step's layers: back-to-back stage-1 launches,
+    # then cold and hot calls.
+    range_detail = {}
+    for name in [w for w in args.range.split(",") if w and w != args.workload]:
+        rw = wl_mod.WORKLOADS[name]
+        if "global" not in rw.layers:
+            continue
+        t_r = time.time()
+        rinp = wl_mod.make_workload_layer(name, "global")
+        rd = rinp.dims
+        bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(
+            torch.bfloat16)
+        rk0, rv0 = bf(rinp.k_pool), bf(rinp.v_pool)
+        del rinp.k_pool, rinp.v_pool
+        rplan = pda.decode_attn_plan(rd["B"], rd["Hq"], rd["Hkv"], rd["D"], rd["S"], rd["M"],
+                                     rd["P"], max_ctx_len=int(rinp.ctx_lens.max()))
+        rspec = rw.layers["global"]
+        rbytes = wl_mod.algorithmic_bytes(rinp.ctx_lens, rspec.num_q_heads, rspec.num_kv_heads,
+                                          rspec.head_dim, rw.page_size, 0)
+        RL = dict(kind="global", inp=rinp, dims=rd, plan=rplan, q=bf(rinp.q),
+                  k=[rk0, rk0.clone()], v=[rv0, rv0.clone()],
+                  bt=torch.from_numpy(rinp.block_table).to(dev),
+                  ctx=torch.from_numpy(rinp.ctx_lens).to(dev),
+                  out=torch.empty((rd["B"], rd["Hq"], rd["D"]), device=dev),
+                  lse=torch.empty((rd["B"], rd["Hq"]), device=dev),
+                  ws=torch.empty(rplan.workspace_bytes, dtype=torch.uint8, device=dev))
+        torch.cuda.synchronize()
+
+        def rcall(L, r):
+            p = L["plan"]
+            pda.decode_attn_global(p, L["q"], L["k"][r], L["v"][r], L["bt"], L["ctx"],
+                                   p.problem.batch, L["inp"].scale, L["out"], L["lse"], L["ws"])
+
+        t_s = time.perf_counter()
+        while (time.perf_counter() - t_s) * 1e3 < args.settle_ms / 2:
+            for i in range(20):
+                rcall(RL, i % 2)
+            torch.cuda.synchronize()
+        rs1_bytes = rbytes - rd["B"] * rd["Hq"] * rd["D"] * 4
+        rs1_us = back_to_back_us(RL, K, stage1_only)
+        rcall_us = back_to_back_us(RL, K, rcall)
+        cold = []
+        for i in range(50):
+            flush_buf.fill_(i & 0xFF)
+            ea, eb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ea.record(stream)
+            rcall(RL, i % 2)
+            eb.record(stream)
+            cold.append((ea, eb))
+        torch.cuda.synchronize()
+        cold = sorted(1e3 * a.elapsed_time(b) for a, b in cold)
+        rtrace = load_trace_mean_us(name)
+        med = cold[len(cold) // 2]
+        range_detail[name] = {
+            "description": rw.description, "num_splits": rplan.num_splits,
+            "layer_algorithmic_bytes": rbytes,
+            "stage1_back_to_back_us": round(rs1_us, 2),
+            "stage1_pct_of_hbm_peak": round(100 * rs1_bytes / (rs1_us * 1e-6) / 1e9 /
+                                            PEAK_HBM_GBS, 2),
+            "stage1_trace_mean_us": rtrace,
+            "stage1_trace_pct_of_hbm_peak": (round(100 * rs1_bytes / (rtrace * 1e-6) / 1e9 /
+                                                   PEAK_HBM_GBS, 2) if rtrace else None),
+            "layer_back_to_back_us": round(rcall_us, 2),
+            "layer_back_to_back_pct_of_hbm_peak": round(100 * rbytes / (rcall_us * 1e-6) / 1e9 /
+                                                        PEAK_HBM_GBS, 2),
+            "us_per_call_median": round(med, 2),
+            "us_per_call_p10": round(cold[len(cold) // 10], 2),
+            "us_per_call_p90": round(cold[(9 * len(cold)) // 10], 2),
+            "pct_of_hbm_peak": round(100 * rbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 2),
+            "setup_s": round(time.time() - t_r, 1)}
+        del RL, rk0, rv0
+        torch.cuda.empty_cache()
+        print("# range %s: %s" % (name, range_detail[name]), file=sys.stderr, flush=True)
+
     step_bytes = sum(L["bytes"] + (L["append_bytes"] if appends else 0) for L in layers)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     s1_ms = [a.elapsed_time(b) for a, b in ev]
@@ -394,9 +556,10 @@ def main() -> int:
     ginp = dominant["inp"]
     gd = dominant["dims"]
     s1_bytes = dominant["bytes"] - gd["B"] * args.q_len * gd["Hq"] * gd["D"] * 4  # minus out
-    achieved = s1_bytes / (s1_avg_us * 1e-6) / 1e9
+    achieved = s1_bytes / (s1_b2b_us * 1e-6) / 1e9
     plain = args.q_len == 1 and args.sink == 0 and not args.k_eq_v
     traffic = load_traffic(args.workload, dominant["plan"].num_splits) if plain else None
+    trace_us = load_trace_mean_us(args.workload) if plain else None
     # Long query chunks (prefill) carry more flops per byte than the MFMA/HBM ridge: then the
     # kernel is priced against the bf16 MFMA peak instead.
     s1_flops = dominant["flops"]
@@ -409,15 +572,23 @@ def main() -> int:
         "unit": "GB/s",
         "frac": round(achieved / PEAK_HBM_GBS, 4),
         "traffic": traffic,
-        "traffic_GB_per_s": (round(traffic / (s1_avg_us * 1e-6) / 1e9, 1)
+        "traffic_GB_per_s": (round(traffic / (s1_b2b_us * 1e-6) / 1e9, 1)
                              if traffic is not None else None),
         "traffic_over_algorithmic": round(traffic / s1_bytes, 4) if traffic is not None else None,
-        "avg_launch_us": round(s1_avg_us, 3),
+        "avg_launch_us": round(s1_b2b_us, 3),
+        "avg_launch_us_source": "%d back-to-back stage-1 launches between one HIP event pair on "
+                                "the launch stream" % K,
+        "event_pair_per_launch_avg_us": round(s1_avg_us, 3),
+        "trace_mean_us": trace_us,
+        "trace_frac": (round(s1_bytes / (trace_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
+                       if trace_us is not None else None),
+        "trace_profile": ("profiles/stage1_global_%s_kernel_trace.txt" % args.workload
+                          if trace_us is not None else None),
         "algorithmic_bytes_per_launch": s1_bytes,
         "algorithmic_flops_per_launch": s1_flops,
     }
     if mfma_bound:
-        tflops = s1_flops / (s1_avg_us * 1e-6) / 1e12
+        tflops = s1_flops / (s1_b2b_us * 1e-6) / 1e12
         roofline.update(bound="mfma", achieved=round(tflops, 1), peak=PEAK_BF16_TFLOPS,
                         unit="TFLOP/s", frac=round(tflops / PEAK_BF16_TFLOPS, 4),
                         hbm_GB_per_s=round(achieved, 1))
@@ -466,6 +637,11 @@ def main() -> int:
         "roofline": roofline,
         "cpu_baseline": None,
         "layers_detail": detail,
+        "global_layer_range": range_detail,
+        "global_layer_cold_pct_of_hbm_peak": dict(
+            [(args.workload, detail["global"]["pct_of_hbm_peak"])] if "global" in detail else [],
+            **{k: v["pct_of_hbm_peak"] for k, v in range_detail.items()}),
+        "provenance": provenance(),
     }
 
     if not args.no_cpu_baseline:

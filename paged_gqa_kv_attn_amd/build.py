@@ -72,7 +72,29 @@ def build(extra_flags=(), out=None, obj_dir=None) -> str:
     if res.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
     os.replace(tmp, lib)
+    if out is None:
+        _write_build_info()
     return lib
+
+
+def _write_build_info() -> None:
+    """Record the source revision next to the library (``_build_info.json``), so that a copy of
+    the tree without its repository still tells which revision the library was built from."""
+    import json
+    root = os.path.dirname(HERE)
+    info = {"git_sha": None, "git_dirty": None}
+    try:
+        sha = subprocess.run(["git", "-C", root, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10)
+        if sha.returncode == 0:
+            dirty = subprocess.run(["git", "-C", root, "status", "--porcelain",
+                                    "--untracked-files=no"], capture_output=True, text=True,
+                                   timeout=10)
+            info = {"git_sha": sha.stdout.strip(), "git_dirty": bool(dirty.stdout.strip())}
+    except (OSError, subprocess.SubprocessError):
+        pass
+    with open(os.path.join(HERE, "_build_info.json"), "w") as f:
+        json.dump(info, f)
 
 
 if __name__ == "__main__":
