@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdecode_attn.so")
 SOURCES = ["decode_attn.cpp", "stage1.hip", "prefill.hip", "stage2.hip", "append.hip",
-           "append_rope.hip", "noalloc.hip"]
+           "append_rope.hip", "noalloc.hip", "stage1_ks.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU instructions are kept out of the generated code.

@@ -11,6 +11,12 @@
 
 #include "internal.h"
 
+// Single-token decode at head_dim 256 with G <= 4 and one split runs on the key-split stage-1
+// kernel (stage1_ks.hip); 0 keeps it on the column-split kernel of stage1.hip (for A/B builds).
+#ifndef DECODE_ATTN_KEYSPLIT
+#define DECODE_ATTN_KEYSPLIT 1
+#endif
+
 namespace decode_attn {
 namespace {
 
@@ -146,9 +152,15 @@ int run_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool
   a.num_qblocks = qblocks_of(p, plan->group_size);
   a.num_splits = plan->num_splits;
   a.scale_log2 = scale * 1.442695040888963407360f;
-  const hipError_t err = stage1_use_prefill(plan->group_size, a.q_len)
-                             ? launch_prefill(a, p.head_dim, plan->group_size, batch, stream)
-                             : launch_stage1(a, p.head_dim, plan->group_size, batch, stream);
+  hipError_t err;
+  if (stage1_use_prefill(plan->group_size, a.q_len))
+    err = launch_prefill(a, p.head_dim, plan->group_size, batch, stream);
+  else if (DECODE_ATTN_KEYSPLIT && plan->num_splits == 1 &&
+           stage1_keysplit_supported(p.head_dim, plan->group_size, a.q_len, a.sink,
+                                     k_pool == v_pool))
+    err = launch_stage1_keysplit(a, plan->group_size, batch, stream);
+  else
+    err = launch_stage1(a, p.head_dim, plan->group_size, batch, stream);
   if (err != hipSuccess) return DECODE_ATTN_ERR_HIP;
   return DECODE_ATTN_OK;
 }
@@ -257,6 +269,14 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
                               : (p.head_dim >= 512 && !p.values_are_keys && !two_row_groups);
   const int64_t target = (one_per_cu ? 1 : 2) * (int64_t)p.num_cus;
   int64_t splits = (target + pairs - 1) / pairs;
+  // Head_dim 256 with G <= 4 and one chunk per (sequence, kv head) runs on the key-split kernel,
+  // whose 8-wave workgroups keep eight tiles in flight: once the pairs alone give every CU a
+  // workgroup, one split (and no merge) beats two (measured on 32 x 8000 keys, 8 KV heads,
+  // window 1024: 42.5 against 47.1 us).
+  if (DECODE_ATTN_KEYSPLIT && pairs >= p.num_cus &&
+      stage1_keysplit_supported(p.head_dim, G, p.q_len, p.window > 0 ? p.sink : 0,
+                                p.values_are_keys != 0))
+    splits = 1;
   int64_t cap = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
   if (cap > p.max_splits) cap = p.max_splits;
   if (cap < 1) cap = 1;

@@ -116,6 +116,12 @@ int attend(const decode_attn_plan_t* plan, int expected_kind, const void* q, con
            float scale, float* out, float* lse_out, void* workspace, uint64_t workspace_bytes,
            void* stream);
 
+// Stage 1 of single-token decode at head_dim 256 with G <= 4 and separate pools, the waves of a
+// workgroup splitting the chunk's tiles (stage1_ks.hip).
+bool stage1_keysplit_supported(int head_dim, int group_size, int q_len, int sink, bool shared);
+hipError_t launch_stage1_keysplit(const Stage1Args& args, int group_size, int batch,
+                                  hipStream_t stream);
+
 // True when a stage-1 kernel is compiled for (head_dim, group_size).
 bool stage1_supported(int head_dim, int group_size);
 

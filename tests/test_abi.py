@@ -74,6 +74,9 @@ def expected_workspace(B, Hq, ns, D, L=1):
     (dict(batch=8, max_pages_per_seq=80, max_ctx_len=1280), 16),      # 16 pairs
     (dict(num_kv_heads=8, head_dim=256, window=1024), 16),            # 65 tiles, 32 pairs
     (dict(num_kv_heads=8, head_dim=256, window=1024, sink=4), 16),    # + 1 sink tile
+    (dict(batch=32, num_kv_heads=8, head_dim=256, window=1024), 1),   # 256 pairs: key split
+    (dict(batch=32, num_kv_heads=8, head_dim=256, window=1024, values_are_keys=1), 2),
+    (dict(batch=32, num_kv_heads=8, head_dim=256, window=1024, sink=4), 2),
     (dict(batch=1, num_kv_heads=8, head_dim=256, window=64, max_ctx_len=8192), 5),  # 5 tiles
     (dict(batch=1, num_kv_heads=8, head_dim=256, window=64, max_ctx_len=8192, sink=40), 8),
     (dict(q_len=4), 64),                                              # 32 rows: 1 block, 2/CU
