@@ -35,9 +35,8 @@ CPU_SAMPLE_FLOPS = 60e9
 CPU_ONE_THREAD_FLOPS = 6e9
 
 
-def kernel_code_hash() -> str:
-    """First 16 hex digits of the SHA-256 of the library's device code (its .hip_fatbin ELF
-    section): host-side edits and comment edits leave it unchanged, kernel edits do not."""
+def _fatbin() -> bytes:
+    """The library's device code: its .hip_fatbin ELF section."""
     import struct
     import paged_gqa_kv_attn_amd as pda
     with open(pda.library_path(), "rb") as f:
@@ -48,8 +47,40 @@ def kernel_code_hash() -> str:
     names = sections[shstrndx][4]
     for name, _, _, _, offset, size in sections:
         if elf[names + name:elf.index(b"\0", names + name)] == b".hip_fatbin":
-            return hashlib.sha256(elf[offset:offset + size]).hexdigest()[:16]
+            return elf[offset:offset + size]
     raise RuntimeError("no device code section in %s" % pda.library_path())
+
+
+# Kernel families whose code-object bundles are hashed on their own (one bundle per source file).
+KERNEL_FAMILIES = ("stage1_kernel", "stage1_ks_kernel", "prefill_kernel", "stage2_kernel",
+                   "append_kernel", "append_rope_kernel")
+
+
+def kernel_code_hash(kernel: str = "") -> str:
+    """First 16 hex digits of the SHA-256 of the library's device code: the whole .hip_fatbin
+    section, or with ``kernel`` only the offload bundles (one per source file) whose code object
+    names that kernel, so a profile of one kernel stays valid while other sources change.
+    Host-side edits and comment edits leave either unchanged, kernel edits do not."""
+    data = _fatbin()
+    if not kernel:
+        return hashlib.sha256(data).hexdigest()[:16]
+    magic = b"__CLANG_OFFLOAD_BUNDLE__"
+    starts = []
+    i = data.find(magic)
+    while i >= 0:
+        starts.append(i)
+        i = data.find(magic, i + 1)
+    h = hashlib.sha256()
+    found = False
+    needle = kernel.encode()
+    for k, a in enumerate(starts):
+        b = starts[k + 1] if k + 1 < len(starts) else len(data)
+        if needle in data[a:b]:
+            h.update(data[a:b])
+            found = True
+    if not found:
+        raise RuntimeError("no code object names %s" % kernel)
+    return h.hexdigest()[:16]
 
 
 def load_traffic(workload: str, num_splits: int):
@@ -63,7 +94,7 @@ def load_traffic(workload: str, num_splits: int):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_code_sha256_16") != kernel_code_hash():
+    if fields.get("kernel_code_sha256_16") != kernel_code_hash("stage1_kernel"):
         return None
     if fields.get("num_splits") != str(num_splits):
         return None
@@ -84,7 +115,7 @@ def load_trace_mean_us(workload: str):
     h = re.search(r"^kernel_code_sha256_16:\s*(\S+)", text, re.M)
     m = re.search(r"^(?:dominant kernel|global stage 1) stage1_kernel.*mean ([0-9.]+) us", text,
                   re.M)
-    if h is None or m is None or h.group(1) != kernel_code_hash():
+    if h is None or m is None or h.group(1) != kernel_code_hash("stage1_kernel"):
         return None
     return float(m.group(1))
 
@@ -737,6 +768,7 @@ def main() -> int:
             "kind": "oracle", "sample": describe(1, k_one, "%.1f s per step" % one)}
 
     result["kernel_code_sha256_16"] = kernel_code_hash()
+    result["kernel_code_sha256_16_by_source"] = {k: kernel_code_hash(k) for k in KERNEL_FAMILIES}
     print(json.dumps(result), flush=True)
     return 0
 
