@@ -339,8 +339,60 @@ def main() -> int:
 
     appends = args.append or args.rope
 
-    def run_layer(L, r, ev_s1=None):
+    # The step's calls prepared once per layer and pool copy (arguments checked and converted once,
+    # one ctypes call each), as a serving loop with fixed buffers makes them. The graph-replay
+    # diagnostic below uses the ordinary calls, which follow torch's current (capture) stream.
+    def prepare_calls(L, r):
         p = L["plan"]
+        c = {}
+        if L["rope"] is not None:
+            ro = L["rope"]
+            c["append"] = pda.decode_attn_append_kv_rope(
+                p, ro["q"], ro["q_out"], ro["k"], ro["v"], L["k"][r], L["v"][r], L["bt"],
+                L["ctx"], p.problem.batch, ro["cs"], ro["max_pos"], p.problem.head_dim, False,
+                pda.NORM_QK, ro["qw"], ro["kw"], None, ro["eps"], prepare=True)
+        else:
+            c["append"] = pda.decode_attn_append_kv(p, L["k_new"], L["v_new"], L["k"][r],
+                                                    L["v"][r], L["bt"], L["ctx"],
+                                                    p.problem.batch, prepare=True)
+        if L is dominant:
+            c["layer"] = pda.decode_attn_global(p, L["q"], L["k"][r], L["v"][r], L["bt"],
+                                                L["ctx"], p.problem.batch, L["inp"].scale,
+                                                L["out"], L["lse"], L["ws"], prepare=True)
+            if p.num_splits > 1:
+                c["s1"] = pda.decode_attn_stage1(p, L["q"], L["k"][r], L["v"][r], L["bt"],
+                                                 L["ctx"], p.problem.batch, L["inp"].scale,
+                                                 L["ws"], prepare=True)
+                c["s2"] = pda.decode_attn_stage2(p, p.problem.batch, L["ws"], L["out"], L["lse"],
+                                                 prepare=True)
+        else:
+            c["layer"] = pda.decode_attn_sliding(p, L["q"], L["k"][r], L["v"][r], L["bt"],
+                                                 L["ctx"], p.problem.batch, p.problem.window,
+                                                 L["inp"].scale, L["out"], L["lse"], L["ws"],
+                                                 prepare=True)
+        return c
+
+    for L in layers:
+        L["pc"] = [prepare_calls(L, r) for r in range(len(L["k"]))]
+
+    def run_layer(L, r, ev_s1=None, prepared=True):
+        p = L["plan"]
+        if prepared:
+            c = L["pc"][r]
+            if appends:
+                c["append"]()
+            if ev_s1 is not None:
+                ev_s1[0].record(stream)
+            if L is dominant and p.num_splits > 1:
+                c["s1"]()
+                if ev_s1 is not None:
+                    ev_s1[1].record(stream)
+                c["s2"]()
+            else:
+                c["layer"]()
+                if ev_s1 is not None:
+                    ev_s1[1].record(stream)
+            return
         if appends:
             append(L, r)
         if L is dominant and p.num_splits == 1:
@@ -403,14 +455,14 @@ def main() -> int:
         with torch.cuda.stream(side):
             for r in range(R):
                 for L in layers:
-                    run_layer(L, r)
+                    run_layer(L, r, prepared=False)
         stream.wait_stream(side)
         graphs = []
         for r in range(R):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for L in layers:
-                    run_layer(L, r)
+                    run_layer(L, r, prepared=False)
             graphs.append(g)
         torch.cuda.synchronize()
         for i in range(args.warmup):

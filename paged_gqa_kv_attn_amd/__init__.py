@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     NORM_V,
     DecodeAttnError,
     Plan,
+    PreparedCall,
     decode_attn_append_kv,
     decode_attn_append_kv_rope,
     decode_attn_global,

@@ -233,6 +233,28 @@ def test_noalloc_rejects_before_touching_the_device(lib):
     assert f(ctypes.byref(s), *args, 512, 0.1, A, None, None) == ERR_SHAPE
 
 
+def test_prepared_call_checks_once_and_reports_status(lib):
+    """A prepared call converts its arguments once and reports the library's status when called."""
+    p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600)
+    ok = binding.decode_attn_global(p, A, A, A, A, A, 0, 0.1, A, None, A, p.workspace_bytes,
+                                    prepare=True)
+    assert isinstance(ok, binding.PreparedCall)
+    ok()  # batch 0: nothing launched
+    ok()
+    bad = binding.decode_attn_global(p, None, A, A, A, A, 1, 0.1, A, None, A, p.workspace_bytes,
+                                     prepare=True)
+    with pytest.raises(binding.DecodeAttnError) as e:
+        bad()
+    assert e.value.status == ERR_NULL
+    s = plan(batch=2, num_kv_heads=8, head_dim=256, window=1024, max_pages_per_seq=100,
+             max_ctx_len=1600)
+    wrong = binding.decode_attn_sliding(s, A, A, A, A, A, 1, 512, 0.1, A, None, A,
+                                        s.workspace_bytes, prepare=True)
+    with pytest.raises(binding.DecodeAttnError) as e:
+        wrong()
+    assert e.value.status == ERR_SHAPE
+
+
 def test_plan_tampering_and_kind(lib):
     p = plan(batch=2, max_pages_per_seq=100, max_ctx_len=1600)
     bad = binding.Plan.from_buffer_copy(p)
