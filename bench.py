@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import struct
 import sys
 import time
 
@@ -37,7 +38,6 @@ CPU_ONE_THREAD_FLOPS = 6e9
 
 def _fatbin() -> bytes:
     """The library's device code: its .hip_fatbin ELF section."""
-    import struct
     import paged_gqa_kv_attn_amd as pda
     with open(pda.library_path(), "rb") as f:
         elf = f.read()
@@ -75,9 +75,18 @@ def kernel_code_hash(kernel: str = "") -> str:
     needle = kernel.encode()
     for k, a in enumerate(starts):
         b = starts[k + 1] if k + 1 < len(starts) else len(data)
-        if needle in data[a:b]:
-            h.update(data[a:b])
-            found = True
+        if needle not in data[a:b]:
+            continue
+        # Bundle: magic, entry count, then (offset, size, triple length, triple) per entry, offsets
+        # from the magic. Only the entries' bytes are hashed (not the alignment padding after them).
+        count, = struct.unpack_from("<Q", data, a + len(magic))
+        pos = a + len(magic) + 8
+        for _ in range(count):
+            off, size, tlen = struct.unpack_from("<QQQ", data, pos)
+            h.update(data[pos + 24:pos + 24 + tlen])
+            h.update(data[a + off:a + off + size])
+            pos += 24 + tlen
+        found = True
     if not found:
         raise RuntimeError("no code object names %s" % kernel)
     return h.hexdigest()[:16]
