@@ -128,11 +128,13 @@ def test_stage1_partials_follow_the_documented_tile_list(D, G, L, window, sink):
                        ref_l.reshape(B, Hq), "query %d split %d" % (i, sp))
 
 
-@pytest.mark.parametrize("ns", [1, 3, 64, 257])
-def test_stage2_merge_matches_oracle(ns):
+@pytest.mark.parametrize("D", [256, 512])
+@pytest.mark.parametrize("ns", [1, 3, 16, 17, 32, 33, 64, 257])
+def test_stage2_merge_matches_oracle(ns, D):
+    """Split counts below, at and above the 16 split groups of the merge, and head dims 256, 512."""
     import torch
     gu.ensure_library()
-    B, Hq, D = 2, 4, 256
+    B, Hq = 2, 4
     inp = make_layer_inputs([40, 40], Hq, 1, D, page_size=16, seed=22)
     plan = gu.make_plan(inp, force_splits=ns)
     rng = np.random.default_rng(ns)
