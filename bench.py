@@ -14,6 +14,7 @@ Steps rotate over copies of the KV pools so that no step finds its K/V in the L2
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
+    python bench.py --copy-rate            # copy bandwidth of hand-written copy kernels
 """
 from __future__ import annotations
 
@@ -183,6 +184,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--copy-rate", action="store_true",
+                    help="run the copy-rate program (1 GiB device copies by hand-written kernels "
+                         "with and without non-temporal loads/stores, and the runtime's copy): "
+                         "the ceiling of a kernel that reads each byte once and writes it once")
     ap.add_argument("--k-eq-v", action="store_true",
                     help="layers whose values are their keys: one pool passed as both K and V")
     ap.add_argument("--q-len", type=int, default=1,
@@ -211,6 +216,15 @@ def main() -> int:
         print("bench.py measures a single GPU; --gpus %d is not supported (the decode-attention "
               "path has no cross-GPU step; run with --gpus 1)" % args.gpus, flush=True)
         return 2
+
+    if args.copy_rate:
+        # A child process of its own, started before this process touches the GPU.
+        import subprocess
+        from paged_gqa_kv_attn_amd import build as hip_build
+        if not os.path.exists(hip_build.COPY_RATE):
+            print("copy_rate is not built (python -m paged_gqa_kv_attn_amd.build)", flush=True)
+            return 2
+        return subprocess.run([hip_build.COPY_RATE]).returncode
 
     import numpy as np
     import torch
@@ -542,11 +556,15 @@ def main() -> int:
         hot = timed_calls(L, 50, flush=False)
         med = us[len(us) // 2]
         if appends:
+            # The append alone, prepared, behind a queue of fills (as for the hot calls), so that
+            # a short append is not timed waiting for the host to enqueue it.
             eva = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(20)]
+            for i in range(8):
+                flush_buf.fill_(i)
             for i, (ea, eb) in enumerate(eva):
                 ea.record(stream)
-                append(L, i % R)
+                L["pc"][i % R]["append"]()
                 eb.record(stream)
             torch.cuda.synchronize()
             ua = sorted(1e3 * ea.elapsed_time(eb) for ea, eb in eva)

@@ -74,7 +74,24 @@ def build(extra_flags=(), out=None, obj_dir=None) -> str:
     os.replace(tmp, lib)
     if out is None:
         _write_build_info()
+        build_copy_rate()
     return lib
+
+
+COPY_RATE = os.path.join(HERE, "copy_rate")
+
+
+def build_copy_rate() -> str:
+    """Compile the standalone copy-rate program (``csrc/copy_rate.hip``, not part of the library):
+    the copy bandwidth the part reaches, which ``bench.py --copy-rate`` reports."""
+    tmp = COPY_RATE + ".tmp%d" % os.getpid()
+    cmd = ([_hipcc(), "-x", "hip"] + [f for f in COMMON_FLAGS if f != "-fPIC"] +
+           [os.path.join(CSRC, "copy_rate.hip"), "-o", tmp])
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed on copy_rate.hip:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    os.replace(tmp, COPY_RATE)
+    return COPY_RATE
 
 
 def _write_build_info() -> None:

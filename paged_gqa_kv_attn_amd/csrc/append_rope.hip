@@ -9,8 +9,7 @@
 // place for both pairings, NeoX halves and GPT-J interleaved pairs (section "内核框架（Helion）").
 //
 // Layout of the work: a row is a q head, a new k head or a new v head of one new token; a wave
-// takes four consecutive rows of a token, four waves per workgroup, the workgroups of one token
-// along grid.y. Each lane holds D / 64 consecutive elements of a row (one 16-byte load at D = 512,
+// takes four consecutive rows (a row group) of a token, four waves per workgroup. Each lane holds D / 64 consecutive elements of a row (one 16-byte load at D = 512,
 // 8 bytes at D = 256), so a row is one coalesced read and one coalesced write, and a wave keeps
 // four rows' loads in flight at once. The RMS is a wave reduction; the NeoX pair partner (element
 // d +- R/2, held by another lane) comes through the wave's LDS rows, the interleaved partner is in
@@ -27,7 +26,30 @@ namespace decode_attn {
 namespace {
 
 constexpr int kRopeWaves = 4;
-constexpr int kRopeRowsPerWave = 4;
+// Rows per wave (D = 512, D = 256), and whether rows are read and written with the non-temporal
+// hint (each row is touched once); build knobs for A/B runs, defaults measured on MI355X.
+#ifndef DECODE_ATTN_ROPE_RW
+#define DECODE_ATTN_ROPE_RW 4
+#endif
+#ifndef DECODE_ATTN_ROPE_RW256
+#define DECODE_ATTN_ROPE_RW256 DECODE_ATTN_ROPE_RW
+#endif
+#ifndef DECODE_ATTN_ROPE_NT
+#define DECODE_ATTN_ROPE_NT 1
+#endif
+constexpr int kRopeRowsPerWave = DECODE_ATTN_ROPE_RW;      // D = 512
+constexpr int kRopeRowsPerWave256 = DECODE_ATTN_ROPE_RW256;  // D = 256
+
+template <typename T>
+__device__ __forceinline__ T load_row(const T* p) {
+  if constexpr (DECODE_ATTN_ROPE_NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <typename T>
+__device__ __forceinline__ void store_row(T v, T* p) {
+  if constexpr (DECODE_ATTN_ROPE_NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
 
 __global__ __launch_bounds__(256) void rope_cache_kernel(float* cos_sin, int64_t count,
                                                          int rotary_dim, int freq_dim,
@@ -128,9 +150,14 @@ __device__ __forceinline__ void row_dst(const AppendRopeArgs& a, RowRef& ref, in
             (((size_t)page * Hkv + g) * a.page_size + slot) * D;
 }
 
-// One workgroup per (new token, 4 * RW rows); wave w takes rows RW * w .. RW * w + RW - 1 of the
-// workgroup's slice. Every global load of a wave (its RW rows, the norm weights, its lanes' cos
-// and sin) is issued before any result is needed, so one memory latency covers the wave's work.
+// Wave w of a workgroup takes RW consecutive rows of one token. With `flat` 0 the grid is
+// (token, slice of its rows); with `flat` 1 (FAST path only, used when a token's row groups do
+// not fill whole workgroups) global wave gw takes row group gw % wpt of token gw / wpt, so that
+// no wave slot idles. Either way workgroups of consecutive tokens are dispatched one after
+// another and the launch streams through q, k_new and v_new in address order. Every global load
+// of a wave (its RW rows, the norm weights, its lanes' cos and sin) is issued before any result
+// is needed, so one memory latency covers the wave's work; the row loads and stores carry the
+// non-temporal hint, as each row is touched once.
 //
 // FAST (chosen on the host when R is a multiple of 2 * D / 64 and the table and weights are
 // 16-byte aligned): a lane's elements are all rotated or all not, and for NeoX all on one side of
@@ -138,7 +165,8 @@ __device__ __forceinline__ void row_dst(const AppendRopeArgs& a, RowRef& ref, in
 // same element of lane +- R / (2 E), fetched with a cross-lane permute (no LDS, no barrier).
 // Otherwise the general path: per-element table loads and the partner through LDS.
 template <int D, int RW, int MODE>
-__global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a) {
+__global__ __launch_bounds__(64 * kRopeWaves)
+void append_rope_kernel(const AppendRopeArgs a, int tokens, int flat) {
   constexpr bool FAST = MODE != 0;
   constexpr int E = D / 64;
   typedef typename RowVec<E>::type vec_t;
@@ -148,15 +176,26 @@ __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a
   // The wave index is the same in all lanes; readfirstlane lets the row bookkeeping below stay in
   // scalar registers and scalar branches.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tok = blockIdx.x;  // b * L + i
-  const int b = tok / a.q_len;
-  const int i = tok - b * a.q_len;
-  const int t = load_uniform(a.ctx_lens, b) - a.q_len + i;
-  if (t < 0 || t >= a.max_position) return;  // the same for the whole workgroup
-
   const bool same = a.v_pool == a.k_pool;
   const int rows_per_token = a.num_q_heads + a.num_kv_heads * (same ? 1 : 2);
-  const int r0 = (blockIdx.y * kRopeWaves + wave) * RW;
+  int tok, r0;  // this wave's token (b * L + i) and first row
+  if (FAST && flat) {
+    // Flat: global wave gw takes row group gw % wpt of token gw / wpt (workgroups span tokens).
+    const int wpt = (rows_per_token + RW - 1) / RW;
+    const int64_t gw = (int64_t)blockIdx.x * kRopeWaves + wave;
+    tok = (int)(gw / wpt);
+    r0 = (int)(gw - (int64_t)tok * wpt) * RW;
+  } else {
+    tok = blockIdx.x;
+    r0 = (blockIdx.y * kRopeWaves + wave) * RW;
+  }
+  const int b = (tok < tokens ? tok : 0) / a.q_len;
+  const int i = (tok < tokens ? tok : 0) - b * a.q_len;
+  const int t = load_uniform(a.ctx_lens, b) - a.q_len + i;
+  // A token at a skipped position, or a wave past the last token, has nothing to do. Without
+  // `flat` this is the same for the whole workgroup; the flat layout is only used by the FAST
+  // path, which has no barrier.
+  if (tok >= tokens || t < 0 || t >= a.max_position) return;
   const int R = a.rotary_dim;
   const int half = R / 2;
   const bool interleaved = MODE == 0 ? a.interleaved != 0 : MODE == 2;
@@ -170,7 +209,7 @@ __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a
   vec_t raw[RW];
 #pragma unroll
   for (int k = 0; k < RW; ++k)
-    raw[k] = reinterpret_cast<const vec_t*>(ref[k].kind >= 0 ? ref[k].src : spare)[lane];
+    raw[k] = load_row(reinterpret_cast<const vec_t*>(ref[k].kind >= 0 ? ref[k].src : spare) + lane);
   bool has_q = false, has_k = false, has_v = false;  // row kinds present in this wave
 #pragma unroll
   for (int k = 0; k < RW; ++k) {
@@ -326,7 +365,7 @@ __global__ __launch_bounds__(256) void append_rope_kernel(const AppendRopeArgs a
     vec_t out;
 #pragma unroll
     for (int e = 0; e < E; e += 2) out[e / 2] = pack_bf16x2(x[k][e], x[k][e + 1]);
-    reinterpret_cast<vec_t*>(ref[k].dst)[lane] = out;
+    store_row(out, reinterpret_cast<vec_t*>(ref[k].dst) + lane);
   }
 }
 
@@ -345,20 +384,33 @@ hipError_t launch_rope_cache(float* cos_sin, int max_position, int rotary_dim, i
 hipError_t launch_append_rope(const AppendRopeArgs& args, int head_dim, int batch,
                               hipStream_t stream) {
   const int rows = args.num_q_heads + args.num_kv_heads * (args.v_pool == args.k_pool ? 1 : 2);
-  constexpr int per_block = kRopeWaves * kRopeRowsPerWave;
-  dim3 grid(batch * args.q_len, (rows + per_block - 1) / per_block);
-  dim3 block(64 * kRopeWaves);
-  void* kargs[] = {const_cast<AppendRopeArgs*>(&args)};
   const auto a16 = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
   const bool fast = args.rotary_dim % (2 * (head_dim / 64)) == 0 && a16(args.cos_sin) &&
                     a16(args.q_weight) && a16(args.k_weight) && a16(args.v_weight);
-  constexpr int RW = kRopeRowsPerWave;
+  int tokens = batch * args.q_len;
+  const int rw = head_dim == 512 ? kRopeRowsPerWave : kRopeRowsPerWave256;
+  const int row_waves = (rows + rw - 1) / rw;
+  // When a token's row groups fill whole workgroups, the 2D grid (token, slice); otherwise the
+  // FAST path deals the row groups out flat so that no wave slot idles (20 rows at D = 512: the
+  // 2D grid would launch 8 waves per token for 5 row groups). Where both fit, the 2D grid
+  // measured faster: dealt flat, 8 row groups per token put every token's q rows on even XCDs and
+  // its k/v rows on odd ones (workgroups go to the XCDs round robin).
+  int flat = fast && row_waves % kRopeWaves != 0;
+  dim3 grid(tokens, (row_waves + kRopeWaves - 1) / kRopeWaves);
+  if (flat) {
+    const int64_t blocks = ((int64_t)tokens * row_waves + kRopeWaves - 1) / kRopeWaves;
+    if (blocks > INT32_MAX) return hipErrorInvalidValue;
+    grid = dim3((unsigned)blocks);
+  }
+  dim3 block(64 * kRopeWaves);
+  void* kargs[] = {const_cast<AppendRopeArgs*>(&args), &tokens, &flat};
+  constexpr int RW = kRopeRowsPerWave, RW2 = kRopeRowsPerWave256;
   // 0: general path; 1: FAST, NeoX pairs; 2: FAST, interleaved pairs.
   const int mode = fast ? (args.interleaved ? 2 : 1) : 0;
   const void* const kernels[2][3] = {
-      {reinterpret_cast<const void*>(&append_rope_kernel<256, RW, 0>),
-       reinterpret_cast<const void*>(&append_rope_kernel<256, RW, 1>),
-       reinterpret_cast<const void*>(&append_rope_kernel<256, RW, 2>)},
+      {reinterpret_cast<const void*>(&append_rope_kernel<256, RW2, 0>),
+       reinterpret_cast<const void*>(&append_rope_kernel<256, RW2, 1>),
+       reinterpret_cast<const void*>(&append_rope_kernel<256, RW2, 2>)},
       {reinterpret_cast<const void*>(&append_rope_kernel<512, RW, 0>),
        reinterpret_cast<const void*>(&append_rope_kernel<512, RW, 1>),
        reinterpret_cast<const void*>(&append_rope_kernel<512, RW, 2>)}};
