@@ -49,7 +49,7 @@ int q_len_of(const decode_attn_problem& p) { return p.q_len > 1 ? p.q_len : 1; }
 
 // Query blocks per (sequence, kv head): a stage-1 workgroup serves 16 or 32 rows of G heads.
 int qblocks_of(const decode_attn_problem& p, int group_size) {
-  return stage1_query_blocks(group_size, q_len_of(p));
+  return stage1_query_blocks(group_size, q_len_of(p), p.head_dim);
 }
 
 // Workspace layout: o_part [B, L, Hq, ns, D] fp32, then (256-byte aligned) lse [B, L, Hq, ns]
@@ -248,7 +248,7 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   // sink keys add their own tiles; the queries of a block widen a window by their count - 1).
   const int64_t max_keys = (int64_t)p.max_pages_per_seq * p.page_size;
   int64_t e = p.max_ctx_len > 0 ? (p.max_ctx_len < max_keys ? p.max_ctx_len : max_keys) : max_keys;
-  const int per_block = stage1_block_queries(G, p.q_len);
+  const int per_block = stage1_block_queries(G, p.q_len, p.head_dim);
   const int64_t span = (int64_t)p.window + (p.q_len < per_block ? p.q_len : per_block) - 1;
   if (p.window > 0 && e > span) e = span;
   int64_t tiles = (e + kTile - 1) / kTile + (p.window > 0 ? 1 : 0);
@@ -262,8 +262,8 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   // Blocks with two row groups (G * q_len > 16) do twice the MFMA and softmax work per tile and
   // likewise run best at two per CU (measured: 4 tokens on the 32K global layer 131 -> 113 us).
   const bool two_row_groups = stage1_row_groups(G, p.q_len) == 2;
-  // Prefill blocks (64 rows, K/V tiles staged in LDS) fit one workgroup per CU at head_dim 512
-  // (133 KB of LDS) and two at 256.
+  // Prefill workgroups (64 rows, or 128 for long head_dim-512 chunks; K/V tiles staged in LDS)
+  // fit one per CU at head_dim 512 (131 KB of LDS) and two at 256.
   const bool one_per_cu = stage1_use_prefill(G, p.q_len)
                               ? p.head_dim >= 512
                               : (p.head_dim >= 512 && !p.values_are_keys && !two_row_groups);

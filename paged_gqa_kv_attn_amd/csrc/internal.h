@@ -136,13 +136,27 @@ inline bool stage1_use_prefill(int group_size, int q_len) {
   return q_len > 1 && group_size * q_len >= kPrefillRows;
 }
 
+// Rows of a prefill workgroup (16 per wave). At head_dim 512, chunks of at least 128 rows per KV
+// head take workgroups of 128 rows: eight waves share each staged tile, two per SIMD. Shorter
+// chunks (no half-empty workgroups), and head_dim 256 (two workgroups per CU), take 64 rows.
+constexpr int kPrefillWideRows = 128;
+#ifndef DECODE_ATTN_PREFILL_WIDE_MIN_ROWS
+#define DECODE_ATTN_PREFILL_WIDE_MIN_ROWS 128
+#endif
+inline int prefill_rows(int head_dim, int group_size, int q_len) {
+  return head_dim == 512 && (int64_t)group_size * q_len >= DECODE_ATTN_PREFILL_WIDE_MIN_ROWS
+             ? kPrefillWideRows
+             : kPrefillRows;
+}
+
 // Queries one stage-1 workgroup serves, and the query blocks of one (sequence, kv head).
-inline int stage1_block_queries(int group_size, int q_len) {
-  if (stage1_use_prefill(group_size, q_len)) return kPrefillRows / group_size;
+inline int stage1_block_queries(int group_size, int q_len, int head_dim) {
+  if (stage1_use_prefill(group_size, q_len))
+    return prefill_rows(head_dim, group_size, q_len) / group_size;
   return 16 * stage1_row_groups(group_size, q_len) / group_size;
 }
-inline int stage1_query_blocks(int group_size, int q_len) {
-  const int per = stage1_block_queries(group_size, q_len);
+inline int stage1_query_blocks(int group_size, int q_len, int head_dim) {
+  const int per = stage1_block_queries(group_size, q_len, head_dim);
   return (q_len + per - 1) / per;
 }
 

@@ -10,22 +10,21 @@
 // What changes against the decode kernel is the shape of the work. Decode has 16-32 (query,
 // head) rows per KV head and streams K/V once, so the decode kernel splits the head dim across
 // its waves and is bound by HBM. A prefill chunk has thousands of rows per KV head, and every
-// K/V tile serves all of them: the work is MFMA-bound. Here a workgroup owns 64 rows (16 per
-// wave, each wave with the full head dim), all waves share one 32-key K/V tile staged in LDS,
-// and no scores cross waves:
+// K/V tile serves all of them: the work is MFMA-bound. Here every wave owns 16 rows with the full
+// head dim, all waves of a workgroup share one 32-key K/V tile staged in LDS, and no scores cross
+// waves. At head_dim 512 a workgroup has 8 waves (128 rows): the double-buffered tiles take
+// 131 KB of LDS, so one workgroup fills a CU, and its 8 waves put two on each SIMD (256
+// registers each), so one wave's softmax and LDS traffic run under the other's MFMAs. At head_dim
+// 256 a workgroup has 4 waves (64 rows) and two fit on a CU.
 //
 //   - K/V tile of the step (32 keys = two 16-key entries of the tile list, each on its own page)
-//     in LDS, double-buffered; the next tile is fetched into registers and written to the other
-//     buffer one step later (one barrier per step). At head_dim 512 the K half of that write
-//     comes first in the step; the score MFMAs then read their K operands eight at a time, and the
-//     V half of the write and the fetch of the tile after it follow them (a wave's LDS accesses
-//     complete in order, so the score reads wait behind the K half only). The loads of that fetch
-//     are spread over the step, K between the score batches and V between the P.V column groups,
-//     so the address unit works while the MFMAs do instead of stalling the wave's issue; they land
-//     directly in AGPRs, which the LDS writes read. Rows are padded by 16 bytes
-//     and 16-byte chunks are XOR-swizzled within 64-byte groups, so the score operand reads (16
-//     keys, same column) and the P.V operand reads (16 column groups, same key) are free of
-//     bank conflicts.
+//     in LDS, double-buffered, one barrier per step. At head_dim 512 the tile goes from memory
+//     straight into LDS (global_load_lds_dwordx4, one key row of 1 KB per wave instruction),
+//     issued right after the barrier into the buffer that step has just released, so it has a
+//     whole step to land; no registers hold it. At head_dim 256 it is fetched into registers and
+//     written to the other buffer at the end of the next step. K rows are padded by 16 bytes and
+//     their 16-byte chunks XOR-swizzled within 64-byte groups, so the score operand reads (16
+//     keys, same column) are free of bank conflicts; V rows (own buffer) are padded by 32 bytes.
 //   - scores: S^T[32 keys][16 rows] per wave with v_mfma_f32_16x16x32_bf16, A = K (keys x 32
 //     columns, from LDS), B = the wave's q rows (in registers for the whole kernel);
 //   - online softmax per row in base 2, exactly as the decode kernel (masks by select, running
@@ -33,8 +32,9 @@
 //   - P.V with v_mfma_f32_16x16x32_bf16: A = P (16 rows x 32 keys) straight from the score
 //     registers; the 32 keys of the MFMA's reduction run in the order the score layout leaves
 //     them (keys 4g..4g+3 then 16+4g..16+4g+3 for lane group g), and B = V takes its keys in that
-//     same order; lane n owns output columns [n*D/16, (n+1)*D/16), so each B read is 16
-//     contiguous bytes of one key row, transposed in the lane with v_perm_b32.
+//     same order through LDS transpose reads (ds_read_b64_tr_b16: 16 columns of 4 keys per read),
+//     MFMA e producing output columns 16e .. 16e + 15. (The earlier form read 16 contiguous bytes
+//     of one key row per lane and transposed them in the lane with v_perm_b32.)
 //
 // Keys outside the union of the block's ranges (and entries past the split) are written to LDS as
 // zeros, so 0 * NaN never reaches P.V; per-row causal, window and sink masks are applied to the
@@ -48,8 +48,6 @@
 namespace decode_attn {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
 constexpr int kStepKeys = 2 * kTile;  // two tile-list entries per loop step
 
 // Build-time knobs of the step's order (defaults measured on MI355X; the alternatives serve A/B
@@ -57,7 +55,9 @@ constexpr int kStepKeys = 2 * kTile;  // two tile-list entries per loop step
 #ifndef DECODE_ATTN_PREFILL_KAHEAD
 #define DECODE_ATTN_PREFILL_KAHEAD 8
 #endif
-constexpr int kKAhead = DECODE_ATTN_PREFILL_KAHEAD;  // score operands read ahead of their MFMAs
+#ifndef DECODE_ATTN_PREFILL_KAHEAD_SHARED
+#define DECODE_ATTN_PREFILL_KAHEAD_SHARED 2
+#endif
 #ifndef DECODE_ATTN_PREFILL_SPLIT_STORE
 #define DECODE_ATTN_PREFILL_SPLIT_STORE 1
 #endif
@@ -73,16 +73,35 @@ constexpr bool kSpreadK = DECODE_ATTN_PREFILL_SPREAD_K;  // K loads issued betwe
 #ifndef DECODE_ATTN_PREFILL_EARLY_STORE
 #define DECODE_ATTN_PREFILL_EARLY_STORE 1  // bit 0: head_dim 512, bit 1: head_dim 256
 #endif
+// P.V's V operand by LDS transpose reads (ds_read_b64_tr_b16) instead of row reads and byte
+// permutes in the VALU.
+#ifndef DECODE_ATTN_PREFILL_TR
+#define DECODE_ATTN_PREFILL_TR 1
+#endif
+constexpr bool kTr = DECODE_ATTN_PREFILL_TR;
+// head_dim 512: the tiles go from memory straight into LDS (global_load_lds_dwordx4, one key row
+// per wave instruction) instead of through registers.
+#ifndef DECODE_ATTN_PREFILL_DMA
+#define DECODE_ATTN_PREFILL_DMA 1
+#endif
+constexpr bool kDma = DECODE_ATTN_PREFILL_DMA;
+#ifndef DECODE_ATTN_PREFILL_XCD
+#define DECODE_ATTN_PREFILL_XCD 1
+#endif
+constexpr bool kXcdRemap = DECODE_ATTN_PREFILL_XCD;  // query blocks of a KV head on one XCD
 
-template <int D>
+template <int D, int ROWS>
 struct PShape {
   static_assert(D == 256 || D == 512, "head_dim");
   static constexpr int kPitch = D + 8;                      // LDS row pitch, bf16
+  static constexpr int kVPitch = kTr ? D + 16 : D + 8;      // V rows (own buffer), bf16
   static constexpr int kChunks = D / 8;                     // 16-byte chunks per key row
-  static constexpr int kSwz = D / 128 - 1;                  // chunk swizzle mask
   static constexpr int kQSteps = D / 32;                    // score MFMAs per 16 keys
   static constexpr int kLaneCols = D / 16;                  // output columns per lane
   static constexpr int kVGroups = kLaneCols / 8;            // 8-column groups per lane
+  static constexpr int kRows = ROWS;                        // (query, head) rows per workgroup
+  static constexpr int kWaves = kRows / 16;                 // 16 rows per wave
+  static constexpr int kThreads = 64 * kWaves;
   static constexpr int kLoads = kStepKeys * kChunks / kThreads;  // 16-B loads per thread per matrix
   static constexpr int kKeysPerPass = kThreads / kChunks;   // key rows one pass of loads covers
 };
@@ -92,30 +111,62 @@ struct PShape {
 // spreads the 16 lanes reading column group n of one key row over all 64 banks.
 template <int D>
 __device__ __forceinline__ int swz(int c) {
-  return c ^ ((c >> 4) & PShape<D>::kSwz);
+  return c ^ ((c >> 4) & (D / 128 - 1));
+}
+
+// 16 bytes per lane from global memory to LDS: lane l's bytes land at l_base + 16 l (l_base
+// wave-uniform), so one instruction fills 1 KB of LDS, checked lane by lane on gfx950.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* l_base) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(l_base), 16, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i gets element (i & 3) of the 4-element
+// rows that lanes 4c + (i >> 2) address, for c = 0..3 (a 4 x 4 transpose of 16-bit elements
+// across each quad of lanes), checked lane by lane on gfx950.
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // SHARED: the pools are one buffer (values are the keys); the V tile is the K tile.
-template <int D, int G, bool SHARED>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
-  using Sh = PShape<D>;
-  constexpr int kMats = SHARED ? 1 : 2;
-  // Where the next tile is staged into LDS: around the score MFMAs (K half before them, V half
-  // after, with the fetch of the tile after it spread over the step; head_dim 512, one wave per
-  // SIMD) or at the end of the step (head_dim 256: two waves per SIMD hide each other's latency,
-  // and the fetch gets the whole step to land).
-  constexpr bool kEarlyStore = (DECODE_ATTN_PREFILL_EARLY_STORE >> (D == 512 ? 0 : 1)) & 1;
+template <int D, int G, bool SHARED, int ROWS>
+__global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
+  using Sh = PShape<D, ROWS>;
+  static_assert(Sh::kThreads == 4 * ROWS, "launch bounds");
+  // Tiles staged through registers (head_dim 256, or head_dim 512 built without direct fetches)
+  // are written to LDS at the end of the step (the fetch gets the whole step to land) or, as an
+  // A/B variant for head_dim 512, around the score MFMAs (K half before them, V half after, the
+  // fetch of the tile after it spread over the step).
+  constexpr bool kDmaD = kDma && D == 512 && ROWS == kPrefillWideRows;
+  constexpr bool kEarlyStore =
+      !kDmaD && ((DECODE_ATTN_PREFILL_EARLY_STORE >> (D == 512 ? 0 : 1)) & 1);
+  // Score operands read ahead of their MFMAs (fewer when one tile serves as K and V).
+  constexpr int kKAhead = SHARED && kDmaD ? DECODE_ATTN_PREFILL_KAHEAD_SHARED
+                                           : DECODE_ATTN_PREFILL_KAHEAD;
   static_assert(Sh::kQSteps % kKAhead == 0 && kKAhead % 2 == 0, "score read-ahead");
-  __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2][kMats][kStepKeys][Sh::kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kStepKeys][Sh::kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][SHARED ? 1 : kStepKeys][Sh::kVPitch];
+  auto KB = [&](int b) -> uint16_t(*)[Sh::kPitch] { return k_lds[b]; };
+  auto VB = [&](int b) -> uint16_t(*)[Sh::kVPitch] { return v_lds[b]; };
 
-  constexpr int kQB = kPrefillRows / G;  // queries per block
+  constexpr int kWaves = Sh::kWaves, kThreads = Sh::kThreads;
+  constexpr int kQB = Sh::kRows / G;  // queries per block
   const int ns = a.num_splits;
-  const int split = (int)blockIdx.x % ns;
+  // Work item of this workgroup: (b, kvh) pair major, then query block, then split. Workgroups
+  // are handed to the 8 XCDs round robin in launch order, so when the grid divides by 8 the
+  // launch index is remapped so that each XCD takes a contiguous run of work items: the query
+  // blocks of one (sequence, KV head), which all read the same K/V, then share the XCD's L2.
+  const int nwg = (int)(gridDim.x * gridDim.y * gridDim.z);
+  const int lin = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  const int w = (kXcdRemap && nwg % 8 == 0) ? (lin % 8) * (nwg / 8) + lin / 8 : lin;
+  const int per_pair = ns * a.num_qblocks;
+  const int split = w % ns;
   // Later queries attend more keys: blocks are numbered from the last one so the longest
   // workgroups are dispatched first.
-  const int qb = a.num_qblocks - 1 - (int)blockIdx.x / ns;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  const int qb = a.num_qblocks - 1 - (w % per_pair) / ns;
+  const int kvh = (w / per_pair) % a.num_kv_heads;
+  const int b = w / per_pair / a.num_kv_heads;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -160,11 +211,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
   const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
 
   if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
-    for (int idx = tid; idx < kPrefillRows * D; idx += kThreads) {
+    for (int idx = tid; idx < Sh::kRows * D; idx += kThreads) {
       const int r = idx / D;
       if (row_valid(r)) a.o_part[(out_row(r) * ns + split) * D + (idx - r * D)] = 0.f;
     }
-    if (tid < kPrefillRows && row_valid(tid)) a.lse_part[out_row(tid) * ns + split] = -INFINITY;
+    if (tid < Sh::kRows && row_valid(tid)) a.lse_part[out_row(tid) * ns + split] = -INFINITY;
     return;
   }
   const int t_last = t_end - 1;
@@ -242,12 +293,15 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
   // Stores the staged tile; keys outside the union are then overwritten with zeros (only entries
   // at the edges of the ranges, or of invalid pages, have any). Returns whether both are full.
   auto store_tile = [&](int buf, int e, const bool* page_ok, int mats) -> bool {
+    // K rows swizzled (score reads: 16 keys, one column); V rows in their own buffer, swizzled
+    // for row reads or plain for transpose reads (16 keys, 16 columns).
+    const int v_chunk = kTr ? ld_chunk : swz<D>(ld_chunk);
 #pragma unroll
     for (int k = 0; k < Sh::kLoads; ++k) {
-      if (mats & 1) *reinterpret_cast<u32x4*>(&kv_lds[buf][0][ld_key(k)][8 * swz<D>(ld_chunk)]) = stk[k];
+      if (mats & 1)
+        *reinterpret_cast<u32x4*>(&KB(buf)[ld_key(k)][8 * swz<D>(ld_chunk)]) = stk[k];
       if constexpr (!SHARED)
-        if (mats & 2)
-          *reinterpret_cast<u32x4*>(&kv_lds[buf][1][ld_key(k)][8 * swz<D>(ld_chunk)]) = stv[k];
+        if (mats & 2) *reinterpret_cast<u32x4*>(&VB(buf)[ld_key(k)][8 * v_chunk]) = stv[k];
     }
     const bool full = entry_full(e, page_ok[0]) && entry_full(e + 1, page_ok[1]);
     if (!full) {
@@ -259,9 +313,44 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
         const bool in = (v < t_end) & page_ok[k < kHalf ? 0 : 1] & (t < n) & ((t >= lo) | (t < sk));
         if (!in) {
           const u32x4 z = {0u, 0u, 0u, 0u};
-          if (mats & 1) *reinterpret_cast<u32x4*>(&kv_lds[buf][0][key][8 * swz<D>(ld_chunk)]) = z;
+          if (mats & 1) *reinterpret_cast<u32x4*>(&KB(buf)[key][8 * swz<D>(ld_chunk)]) = z;
           if constexpr (!SHARED)
-            if (mats & 2) *reinterpret_cast<u32x4*>(&kv_lds[buf][1][key][8 * swz<D>(ld_chunk)]) = z;
+            if (mats & 2) *reinterpret_cast<u32x4*>(&VB(buf)[key][8 * v_chunk]) = z;
+        }
+      }
+    }
+    return full;
+  };
+
+  // Direct staging (head_dim 512): wave w fetches key rows 8 w .. 8 w + 7 of the step's two
+  // entries (rows 0-15 entry e, 16-31 entry e + 1), K and V, one instruction per row; lane l
+  // fetches the 16-byte chunk that belongs in slot l of the row (swizzled for K, in order for V).
+  auto issue_dma = [&](int b2, int e, int pid0, int pid1, bool* page_ok) {
+    const size_t base0 = entry_base(e, pid0, page_ok[0]);
+    const size_t base1 = entry_base(e + 1, pid1, page_ok[1]);
+#pragma unroll
+    for (int j = 0; j < kStepKeys / kWaves; ++j) {
+      const int r = (kStepKeys / kWaves) * wave + j;
+      const size_t rb = (r < kTile ? base0 : base1) + (size_t)(r % kTile) * D;
+      dma16(a.k_pool + rb + 8 * swz<D>(lane), &KB(b2)[r][0]);
+      if constexpr (!SHARED) dma16(a.v_pool + rb + 8 * lane, &VB(b2)[r][0]);
+    }
+  };
+  // Once this thread's fetches have landed: zeros over the rows it fetched whose key is outside
+  // the union (or on an invalid page). Returns whether both entries are full.
+  auto dma_zero = [&](int b2, int e, const bool* page_ok) -> bool {
+    const bool full = entry_full(e, page_ok[0]) && entry_full(e + 1, page_ok[1]);
+    if (!full) {
+#pragma unroll
+      for (int j = 0; j < kStepKeys / kWaves; ++j) {
+        const int r = (kStepKeys / kWaves) * wave + j;
+        const int v = e + r / kTile;
+        const int t = phys_tile(v < t_end ? v : t_last) * kTile + r % kTile;
+        const bool in = (v < t_end) & page_ok[r / kTile] & (t < n) & ((t >= lo) | (t < sk));
+        if (!in) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(&KB(b2)[r][8 * lane]) = z;
+          if constexpr (!SHARED) *reinterpret_cast<u32x4*>(&VB(b2)[r][8 * lane]) = z;
         }
       }
     }
@@ -282,14 +371,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
 
   // Prologue: tile of step 0 into LDS buffer 0, the tile of step 1 in flight.
   bool ok_cur[2], ok_next[2], ok_nxt[2];
-  issue_loads(t_begin, entry_pid(t_begin), entry_pid(t_begin + 1), ok_next, 3);
-  int32_t pid_next = pid_vector(t_begin + 2);
-  bool full_cur = store_tile(0, t_begin, ok_next, 3);
-  ok_cur[0] = ok_next[0];
-  ok_cur[1] = ok_next[1];
-  issue_loads(t_begin + 2, __builtin_amdgcn_readlane(pid_next, 0),
-              __builtin_amdgcn_readlane(pid_next, 1), ok_next, 3);
-  pid_next = pid_vector(t_begin + 4);
+  int32_t pid_next;
+  bool full_cur;
+  if constexpr (kDmaD) {
+    issue_dma(0, t_begin, entry_pid(t_begin), entry_pid(t_begin + 1), ok_cur);
+    pid_next = pid_vector(t_begin + 2);
+    __builtin_amdgcn_s_waitcnt(0);
+    full_cur = dma_zero(0, t_begin, ok_cur);
+    issue_dma(1, t_begin + 2, __builtin_amdgcn_readlane(pid_next, 0),
+              __builtin_amdgcn_readlane(pid_next, 1), ok_nxt);
+    pid_next = pid_vector(t_begin + 4);
+  } else {
+    issue_loads(t_begin, entry_pid(t_begin), entry_pid(t_begin + 1), ok_next, 3);
+    pid_next = pid_vector(t_begin + 2);
+    full_cur = store_tile(0, t_begin, ok_next, 3);
+    ok_cur[0] = ok_next[0];
+    ok_cur[1] = ok_next[1];
+    issue_loads(t_begin + 2, __builtin_amdgcn_readlane(pid_next, 0),
+                __builtin_amdgcn_readlane(pid_next, 1), ok_next, 3);
+    pid_next = pid_vector(t_begin + 4);
+  }
   __syncthreads();
 
   float m_run = -INFINITY;  // running max (base 2) of row my_row
@@ -324,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
 #pragma unroll
         for (int c = 0; c < kKAhead; ++c)
           kk[c] = *reinterpret_cast<const bf16x8*>(
-              &kv_lds[buf][0][kTile * g + col][8 * swz<D>(4 * (c0 + c) + grp)]);
+              &KB(buf)[kTile * g + col][8 * swz<D>(4 * (c0 + c) + grp)]);
         if constexpr (kEarlyStore && kSplitStore && kSpreadK) {
           // A share of the next-but-one tile's K loads behind this batch's LDS reads.
           constexpr int kBatches = 2 * Sh::kQSteps / kKAhead;
@@ -421,46 +522,86 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
                       pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
     const bf16x8 pop = __builtin_bit_cast(bf16x8, pa);
 
-    // P.V: lane (col, grp) reads, for each 8-column group cg of its columns, the 8 keys of its
-    // reduction slots (key rows 4 * grp + j and 16 + 4 * grp + j, j < 4) and transposes them
-    // into 8 B operands (one per column).
-    constexpr int kV = SHARED ? 0 : 1;
+    if constexpr (kTr) {
+      // P.V by transpose reads: MFMA e covers output columns 16 e .. 16 e + 15, lane (col, grp)
+      // column 16 e + col. Lane col of group grp addresses key row 4 grp + col / 4 (then
+      // 16 + 4 grp + col / 4), columns 16 e + 4 (col % 4) .. + 3; the transpose hands it
+      // keys 4 grp + c (then 16 + 4 grp + c), c < 4, of its own column: B's reduction slots
+      // 8 grp + j in P's key order.
+      const int r1 = 4 * grp + (col >> 2);
+      const uint16_t* const v1 = SHARED ? &KB(buf)[r1][0] : &VB(buf)[r1][0];
+      const uint16_t* const v2 = SHARED ? &KB(buf)[kTile + r1][0] : &VB(buf)[kTile + r1][0];
 #pragma unroll
-    for (int cg = 0; cg < Sh::kVGroups; ++cg) {
-      const int chunk = swz<D>(col * Sh::kVGroups + cg);
-      u32x4 vr[8];
+      for (int cg = 0; cg < Sh::kVGroups; ++cg) {
+        u32x2 lo[8], hi[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = (j < 4 ? 0 : kTile) + 4 * grp + (j & 3);
-        vr[j] = *reinterpret_cast<const u32x4*>(&kv_lds[buf][kV][key][8 * chunk]);
+        for (int x = 0; x < 8; ++x) {
+          const int d = 16 * (8 * cg + x) + 4 * (col & 3);
+          const int off = SHARED ? 8 * swz<D>(d >> 3) + (d & 7) : d;
+          lo[x] = lds_read_tr16(v1 + off);
+          hi[x] = lds_read_tr16(v2 + off);
+        }
+        if constexpr (kEarlyStore && kSplitStore && kSpreadV) {
+          constexpr int kPer = (Sh::kLoads + Sh::kVGroups - 1) / Sh::kVGroups;
+          issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
+                      __builtin_amdgcn_readlane(pid_next, 1), ok_next, 2, cg * kPer,
+                      cg * kPer + kPer);
+          if (cg == Sh::kVGroups - 1) pid_next = pid_vector(e0 + 6);
+        }
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const u32x4 bv = {lo[x][0], lo[x][1], hi[x][0], hi[x][1]};
+          const int e = 8 * cg + x;
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, __builtin_bit_cast(bf16x8, bv),
+                                                           acc[e], 0, 0, 0);
+        }
       }
-      if constexpr (kEarlyStore && kSplitStore && kSpreadV) {
-        // A share of the next-but-one tile's V loads between the P.V column groups, behind this
-        // group's LDS reads.
-        constexpr int kPer = (Sh::kLoads + Sh::kVGroups - 1) / Sh::kVGroups;
-        issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
-                    __builtin_amdgcn_readlane(pid_next, 1), ok_next, 2, cg * kPer, cg * kPer + kPer);
-        if (cg == Sh::kVGroups - 1) pid_next = pid_vector(e0 + 6);
-      }
+    } else {
+      // P.V: lane (col, grp) reads, for each 8-column group cg of its columns, the 8 keys of its
+      // reduction slots (key rows 4 * grp + j and 16 + 4 * grp + j, j < 4) and transposes them
+      // into 8 B operands (one per column).
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const u32x4 be = {__builtin_amdgcn_perm(vr[1][d], vr[0][d], 0x05040100u),
-                          __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x05040100u),
-                          __builtin_amdgcn_perm(vr[5][d], vr[4][d], 0x05040100u),
-                          __builtin_amdgcn_perm(vr[7][d], vr[6][d], 0x05040100u)};
-        const u32x4 bo = {__builtin_amdgcn_perm(vr[1][d], vr[0][d], 0x07060302u),
-                          __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x07060302u),
-                          __builtin_amdgcn_perm(vr[5][d], vr[4][d], 0x07060302u),
-                          __builtin_amdgcn_perm(vr[7][d], vr[6][d], 0x07060302u)};
-        const int e = 8 * cg + 2 * d;
-        acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, __builtin_bit_cast(bf16x8, be),
-                                                         acc[e], 0, 0, 0);
-        acc[e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            pop, __builtin_bit_cast(bf16x8, bo), acc[e + 1], 0, 0, 0);
+      for (int cg = 0; cg < Sh::kVGroups; ++cg) {
+        const int chunk = swz<D>(col * Sh::kVGroups + cg);
+        u32x4 vr[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = (j < 4 ? 0 : kTile) + 4 * grp + (j & 3);
+          vr[j] = *reinterpret_cast<const u32x4*>(SHARED ? &KB(buf)[key][8 * chunk]
+                                                         : &VB(buf)[key][8 * chunk]);
+        }
+        if constexpr (kEarlyStore && kSplitStore && kSpreadV) {
+          // A share of the next-but-one tile's V loads between the P.V column groups, behind this
+          // group's LDS reads.
+          constexpr int kPer = (Sh::kLoads + Sh::kVGroups - 1) / Sh::kVGroups;
+          issue_loads(e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
+                      __builtin_amdgcn_readlane(pid_next, 1), ok_next, 2, cg * kPer,
+                      cg * kPer + kPer);
+          if (cg == Sh::kVGroups - 1) pid_next = pid_vector(e0 + 6);
+        }
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const u32x4 be = {__builtin_amdgcn_perm(vr[1][d], vr[0][d], 0x05040100u),
+                            __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x05040100u),
+                            __builtin_amdgcn_perm(vr[5][d], vr[4][d], 0x05040100u),
+                            __builtin_amdgcn_perm(vr[7][d], vr[6][d], 0x05040100u)};
+          const u32x4 bo = {__builtin_amdgcn_perm(vr[1][d], vr[0][d], 0x07060302u),
+                            __builtin_amdgcn_perm(vr[3][d], vr[2][d], 0x07060302u),
+                            __builtin_amdgcn_perm(vr[5][d], vr[4][d], 0x07060302u),
+                            __builtin_amdgcn_perm(vr[7][d], vr[6][d], 0x07060302u)};
+          const int e = 8 * cg + 2 * d;
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pop, __builtin_bit_cast(bf16x8, be),
+                                                           acc[e], 0, 0, 0);
+          acc[e + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              pop, __builtin_bit_cast(bf16x8, bo), acc[e + 1], 0, 0, 0);
+        }
       }
     }
 
-    if constexpr (!kEarlyStore) {  // stage the next tile and fetch the one after it here
+    if constexpr (kDmaD) {  // the next tile has landed in the other buffer: mask its edges
+      __builtin_amdgcn_s_waitcnt(0);
+      full_nxt = dma_zero(buf ^ 1, e0 + 2, ok_nxt);
+    } else if constexpr (!kEarlyStore) {  // stage the next tile and fetch the one after it here
       full_nxt = store_tile(buf ^ 1, e0 + 2, ok_next, 3);
       ok_nxt[0] = ok_next[0];
       ok_nxt[1] = ok_next[1];
@@ -473,6 +614,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     ok_cur[0] = ok_nxt[0];
     ok_cur[1] = ok_nxt[1];
     __syncthreads();
+    if constexpr (kDmaD) {  // this buffer is free: the tile after the next one into it
+      issue_dma(buf, e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
+                __builtin_amdgcn_readlane(pid_next, 1), ok_nxt);
+      pid_next = pid_vector(e0 + 6);
+    }
     buf ^= 1;
   }
 
@@ -484,12 +630,19 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
     const float lh = __shfl(l_run, 4 * grp + i);
     const float inv = lh > 0.f ? 1.f / lh : 0.f;
     if (row_valid(r)) {
-      float* dst = a.o_part + (out_row(r) * ns + split) * D + col * Sh::kLaneCols;
+      float* const row_out = a.o_part + (out_row(r) * ns + split) * D;
+      if constexpr (kTr) {
+        // Column 16 e + col: the 16 lanes of a group write 64 contiguous bytes per e.
 #pragma unroll
-      for (int e = 0; e < Sh::kLaneCols; e += 4) {
-        const f32x4 v4 = {acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv,
-                          acc[e + 3][i] * inv};
-        *reinterpret_cast<f32x4*>(dst + e) = v4;
+        for (int e = 0; e < Sh::kLaneCols; ++e) row_out[16 * e + col] = acc[e][i] * inv;
+      } else {
+        float* dst = row_out + col * Sh::kLaneCols;
+#pragma unroll
+        for (int e = 0; e < Sh::kLaneCols; e += 4) {
+          const f32x4 v4 = {acc[e][i] * inv, acc[e + 1][i] * inv, acc[e + 2][i] * inv,
+                            acc[e + 3][i] * inv};
+          *reinterpret_cast<f32x4*>(dst + e) = v4;
+        }
       }
     }
   }
@@ -499,24 +652,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(const Stage1Args a) {
   }
 }
 
-template <int D, int G>
+template <int D, int G, int ROWS>
 hipError_t launch(const Stage1Args& args, bool shared, int batch, hipStream_t stream) {
   dim3 grid(args.num_splits * args.num_qblocks, args.num_kv_heads, batch);
   void* kargs[] = {const_cast<Stage1Args*>(&args)};
-  const void* fn = shared ? reinterpret_cast<const void*>(&prefill_kernel<D, G, true>)
-                          : reinterpret_cast<const void*>(&prefill_kernel<D, G, false>);
-  return hipLaunchKernel(fn, grid, dim3(kThreads), kargs, 0, stream);
+  const void* fn = shared ? reinterpret_cast<const void*>(&prefill_kernel<D, G, true, ROWS>)
+                          : reinterpret_cast<const void*>(&prefill_kernel<D, G, false, ROWS>);
+  return hipLaunchKernel(fn, grid, dim3(PShape<D, ROWS>::kThreads), kargs, 0, stream);
+}
+
+template <int D, int G>
+hipError_t launch_rows(const Stage1Args& args, bool shared, int batch, hipStream_t stream) {
+  if constexpr (D == 512)
+    if (prefill_rows(D, G, args.q_len) == kPrefillWideRows)
+      return launch<D, G, kPrefillWideRows>(args, shared, batch, stream);
+  return launch<D, G, kPrefillRows>(args, shared, batch, stream);
 }
 
 template <int D>
 hipError_t launch_d(const Stage1Args& args, int group_size, bool shared, int batch,
                     hipStream_t stream) {
   switch (group_size) {
-    case 1: return launch<D, 1>(args, shared, batch, stream);
-    case 2: return launch<D, 2>(args, shared, batch, stream);
-    case 4: return launch<D, 4>(args, shared, batch, stream);
-    case 8: return launch<D, 8>(args, shared, batch, stream);
-    case 16: return launch<D, 16>(args, shared, batch, stream);
+    case 1: return launch_rows<D, 1>(args, shared, batch, stream);
+    case 2: return launch_rows<D, 2>(args, shared, batch, stream);
+    case 4: return launch_rows<D, 4>(args, shared, batch, stream);
+    case 8: return launch_rows<D, 8>(args, shared, batch, stream);
+    case 16: return launch_rows<D, 16>(args, shared, batch, stream);
     default: return hipErrorInvalidValue;
   }
 }

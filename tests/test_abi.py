@@ -86,9 +86,9 @@ def expected_workspace(B, Hq, ns, D, L=1):
           q_len=8), 64),                                              # G 4: capped by tiles
     (dict(batch=1, num_q_heads=4, num_kv_heads=1, max_pages_per_seq=64, max_ctx_len=1024), 64),
     (dict(batch=1, max_pages_per_seq=4, max_ctx_len=64), 4),          # capped: >= 1 tile/split
-    (dict(q_len=16), 16),                                             # 2 prefill blocks of 8
-    (dict(q_len=512), 1),                                             # prefill chunk: 64 blocks
-    (dict(batch=1, q_len=64, max_ctx_len=4096), 16),                  # 8 blocks, 256 tiles
+    (dict(q_len=16), 32),                                             # 1 prefill block of 16
+    (dict(q_len=512), 1),                                             # prefill chunk: 32 blocks
+    (dict(batch=1, q_len=64, max_ctx_len=4096), 32),                  # 4 blocks of 128 rows
     (dict(batch=1, num_kv_heads=8, head_dim=256, window=1024, q_len=256), 8),  # 8 x 8 blocks
     (dict(num_q_heads=8, num_kv_heads=1), 64),                        # TP2 share of 4 x 33792
     (dict(num_q_heads=8, num_kv_heads=4, head_dim=256, window=1024), 32),  # its sliding layer

@@ -33,7 +33,7 @@ def test_prefill_small_shapes(D, G, L, window):
         gu.compare(out, lse, *ref, "prefill D%d G%d L%d W%d ns%d" % (D, G, L, window, splits))
 
 
-@pytest.mark.parametrize("L", [512, 1024])
+@pytest.mark.parametrize("L", [1024, 1280])
 def test_prefill_one_split_chunks(L):
     """Chunks large enough that the query blocks fill the GPU: the plan has one split, stage 1
     writes out and lse in place and stage 2 is skipped."""
@@ -51,7 +51,7 @@ def test_prefill_one_split_without_lse_output():
     import torch
     import paged_gqa_kv_attn_amd as pda
     gu.ensure_library()
-    inp = make_layer_inputs([600, 813], 16, 2, 512, page_size=16, seed=73, q_len=600)
+    inp = make_layer_inputs([1100, 1313], 16, 2, 512, page_size=16, seed=73, q_len=1100)
     plan = gu.make_plan(inp)
     assert plan.num_splits == 1
     d = inp.dims

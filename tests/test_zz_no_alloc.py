@@ -61,6 +61,6 @@ def test_noalloc_multi_token_then_one_split_chunk():
     prefill chunk whose layer call keeps only its lse plane in the array."""
     first = make_layer_inputs([5000, 6001], 16, 2, 512, seed=91, q_len=4)
     p1 = _check(first, "q_len 4")
-    second = make_layer_inputs([600, 813], 16, 2, 512, seed=92, q_len=600)
+    second = make_layer_inputs([1100, 1313], 16, 2, 512, seed=92, q_len=1100)
     p2 = _check(second, "prefill chunk")
     assert p2.num_splits == 1 and p2.layer_workspace_bytes < p1.layer_workspace_bytes
