@@ -153,3 +153,25 @@ def test_prefill_sliding_values_equal_keys():
     t["v"] = t["k"]
     out, lse = gu.run(inp, dev_bufs=t, values_are_keys=True)
     gu.compare(out, lse, *gu.reference(inp), "prefill sliding k=v")
+
+
+@pytest.mark.parametrize("D,G,L", [(512, 8, 64), (512, 2, 40), (256, 2, 64)])
+def test_prefill_invalid_first_page_is_skipped(D, G, L):
+    """A block-table entry outside [0, P) on the first page of a sequence: its 16 keys are
+    skipped, so the chunk equals the same queries over the sequence without that page (block
+    table shifted by one page, context 16 keys shorter: the same keys at the same causal offsets).
+    Covers the zero-filled tiles of the direct-to-LDS fetch (head_dim 512, 128-row workgroups)
+    and of the register-staged paths."""
+    import oracle
+    print("prefill invalid first page D=%d G=%d L=%d" % (D, G, L), flush=True)
+    Hkv = 2
+    inp = make_layer_inputs([400, 300], G * Hkv, Hkv, D, page_size=16, seed=[79, D, G, L],
+                            q_mult=1.5, q_len=L)
+    inp.block_table[0, 0] = inp.k_pool.shape[0] + 5
+    inp.block_table[1, 0] = -7
+    ref = oracle.decode_attn_multi(inp.q, inp.k_pool, inp.v_pool,
+                                   np.ascontiguousarray(inp.block_table[:, 1:]),
+                                   inp.ctx_lens - 16, inp.scale)
+    for splits in (0, 3):
+        out, lse = gu.run(inp, force_splits=splits)
+        gu.compare(out, lse, *ref, "prefill invalid page D%d G%d L%d ns%d" % (D, G, L, splits))
