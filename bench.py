@@ -199,6 +199,10 @@ def main() -> int:
     ap.add_argument("--rope", action="store_true",
                     help="each layer call first runs the fused QK-norm + RoPE + paged append of the "
                          "step's new tokens, then attends with the rotated q")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the two extra lines of the default run: the global layer on a "
+                         "512-token prefill chunk per sequence (MFMA-bound) and the fused QK-norm "
+                         "+ RoPE + append of a 2048-token chunk per sequence")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay diagnostic after the timed region")
     ap.add_argument("--sink", type=int, default=0,
@@ -512,17 +516,22 @@ def main() -> int:
             pda.decode_attn_stage1(p, L["q"], L["k"][r], L["v"][r], L["bt"], L["ctx"],
                                    p.problem.batch, L["inp"].scale, L["ws"])
 
-    def back_to_back_us(L, n, fn):
+    def back_to_back_us(L, n, fn, batches=5):
+        """Mean launch duration of n back-to-back launches between one HIP event pair; the median
+        over `batches` such batches (one batch can catch a clock or memory-controller hiccup)."""
         for i in range(3):
             fn(L, i % len(L["k"]))
-        ba, bb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        ba.record(stream)
-        for i in range(n):
-            fn(L, i % len(L["k"]))
-        bb.record(stream)
-        torch.cuda.synchronize()
-        return 1e3 * ba.elapsed_time(bb) / n
+        per = []
+        for _ in range(batches):
+            ba, bb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            ba.record(stream)
+            for i in range(n):
+                fn(L, i % len(L["k"]))
+            bb.record(stream)
+            torch.cuda.synchronize()
+            per.append(1e3 * ba.elapsed_time(bb) / n)
+        return sorted(per)[len(per) // 2]
 
     s1_b2b_us = back_to_back_us(dominant, K, stage1_only)
 
@@ -656,6 +665,79 @@ def main() -> int:
         torch.cuda.empty_cache()
         print("# range %s: %s" % (name, range_detail[name]), file=sys.stderr, flush=True)
 
+    # Extras of the plain run, on the global layer's pools (after the step's timing): a prefill
+    # chunk of 512 tokens per sequence (the layer call: one split, stage 1 writes out and lse
+    # in place) and the fused QK-norm + RoPE + append of 2048 tokens per sequence (into copies of
+    # the pools), each timed over back-to-back launches between one HIP event pair.
+    extras = {}
+    if not args.no_extras and args.q_len == 1 and not appends and not args.k_eq_v and \
+            args.sink == 0 and dominant["kind"] == "global":
+        t_x = time.time()
+        gL = dominant
+        gd, ginp0 = gL["dims"], gL["inp"]
+        B_, Hq_, Hkv_, D_ = gd["B"], gd["Hq"], gd["Hkv"], gd["D"]
+        mx = int(ginp0.ctx_lens.max())
+
+        def b2b(fn, n, warm=2):
+            for _ in range(warm):
+                fn()
+            xa, xb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            xa.record(stream)
+            for _ in range(n):
+                fn()
+            xb.record(stream)
+            torch.cuda.synchronize()
+            return 1e3 * xa.elapsed_time(xb) / n
+
+        PLq = 512
+        pplan = pda.decode_attn_plan(B_, Hq_, Hkv_, D_, gd["S"], gd["M"], gd["P"],
+                                     max_ctx_len=mx, q_len=PLq)
+        pq = bf(wl_mod.make_new_tokens(B_, PLq, Hq_, Hkv_, D_, seed=[wl.index, 11],
+                                       scale=1.0)["q"])
+        pout = torch.empty((B_, PLq, Hq_, D_), device=dev)
+        plse = torch.empty((B_, PLq, Hq_), device=dev)
+        pws = torch.empty(max(pplan.layer_workspace_bytes, 256), dtype=torch.uint8, device=dev)
+        pcall = pda.decode_attn_global(pplan, pq, gL["k"][0], gL["v"][0], gL["bt"], gL["ctx"], B_,
+                                       ginp0.scale, pout, plse, pws, prepare=True)
+        p_us = b2b(pcall, 5)
+        p_flops = wl_mod.algorithmic_flops(ginp0.ctx_lens, Hq_, D_, 0, 0, q_len=PLq)
+        extras["prefill_chunk"] = {
+            "description": "global layer, %d causal query tokens per sequence at the end of each "
+                           "context (layer call)" % PLq,
+            "num_splits": pplan.num_splits, "us_per_call": round(p_us, 1),
+            "algorithmic_flops": p_flops,
+            "TFLOP_per_s": round(p_flops / (p_us * 1e-6) / 1e12, 1),
+            "pct_of_bf16_mfma_peak": round(100 * p_flops / (p_us * 1e-6) / 1e12 /
+                                           PEAK_BF16_TFLOPS, 2)}
+        del pq, pout, plse, pws, pcall
+        RLq = 2048
+        rplan_x = pda.decode_attn_plan(B_, Hq_, Hkv_, D_, gd["S"], gd["M"], gd["P"],
+                                       max_ctx_len=mx, q_len=RLq)
+        nt = wl_mod.make_new_tokens(B_, RLq, Hq_, Hkv_, D_, seed=[wl.index, 12])
+        cs = torch.empty((mx + 1, D_), dtype=torch.float32, device=dev)
+        pda.decode_attn_rope_cache(cs, mx + 1, D_, 1e6)
+        f32 = lambda a: torch.from_numpy(a).to(dev)
+        rq_in, rk_in, rv_in = bf(nt["q"]), bf(nt["k"]), bf(nt["v"])
+        rq_out = torch.empty_like(rq_in)
+        kc, vc = gL["k"][0].clone(), gL["v"][0].clone()
+        rcall_x = pda.decode_attn_append_kv_rope(
+            rplan_x, rq_in, rq_out, rk_in, rv_in, kc, vc, gL["bt"], gL["ctx"], B_, cs, mx + 1, D_,
+            False, pda.NORM_QK, f32(nt["q_weight"]), f32(nt["k_weight"]), None, 1e-6,
+            prepare=True)
+        r_us = b2b(rcall_x, 10)
+        r_bytes = B_ * RLq * (4 * Hq_ * D_ + 8 * Hkv_ * D_ + 4 * D_)
+        extras["rope_append_chunk"] = {
+            "description": "fused QK-norm + RoPE + paged append of %d new tokens per sequence "
+                           "(global layer: q, k and v rows, full NeoX rotation)" % RLq,
+            "us_per_call": round(r_us, 2), "algorithmic_bytes": r_bytes,
+            "GB_per_s": round(r_bytes / (r_us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * r_bytes / (r_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 2)}
+        del rq_in, rk_in, rv_in, rq_out, kc, vc, cs, rcall_x
+        torch.cuda.empty_cache()
+        extras["setup_and_timing_s"] = round(time.time() - t_x, 1)
+        print("# extras: %s" % extras, file=sys.stderr, flush=True)
+
     step_bytes = sum(L["bytes"] + (L["append_bytes"] if appends else 0) for L in layers)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     s1_ms = [a.elapsed_time(b) for a, b in ev]
@@ -686,8 +768,8 @@ def main() -> int:
                              if traffic is not None else None),
         "traffic_over_algorithmic": round(traffic / s1_bytes, 4) if traffic is not None else None,
         "avg_launch_us": round(s1_b2b_us, 3),
-        "avg_launch_us_source": "%d back-to-back stage-1 launches between one HIP event pair on "
-                                "the launch stream" % K,
+        "avg_launch_us_source": "median over 5 batches of %d back-to-back stage-1 launches, each "
+                                "batch between one HIP event pair on the launch stream" % K,
         "event_pair_per_launch_avg_us": round(s1_avg_us, 3),
         "trace_mean_us": trace_us,
         "trace_frac": (round(s1_bytes / (trace_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)
@@ -748,6 +830,7 @@ def main() -> int:
         "cpu_baseline": None,
         "layers_detail": detail,
         "global_layer_range": range_detail,
+        "extras": extras,
         "global_layer_cold_pct_of_hbm_peak": dict(
             [(args.workload, detail["global"]["pct_of_hbm_peak"])] if "global" in detail else [],
             **{k: v["pct_of_hbm_peak"] for k, v in range_detail.items()}),
