@@ -615,12 +615,17 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     ok_cur[1] = ok_nxt[1];
     __syncthreads();
     if constexpr (kDmaD) {  // this buffer is free: the tile after the next one into it
+      // (Past the split's last entry this re-fetches that entry's rows, in bounds and unused;
+      // issuing it unconditionally keeps the compiler from waiting for it before the next
+      // step's LDS reads, which it does when the fetch sits under a branch.)
       issue_dma(buf, e0 + 4, __builtin_amdgcn_readlane(pid_next, 0),
                 __builtin_amdgcn_readlane(pid_next, 1), ok_nxt);
       pid_next = pid_vector(e0 + 6);
     }
     buf ^= 1;
   }
+  // No fetch into LDS may still be landing when the workgroup ends and its LDS is reassigned.
+  if constexpr (kDmaD) __builtin_amdgcn_s_waitcnt(0);
 
   // Normalise and write: lane (col, grp) holds rows 16 * wave + 4 * grp + i, columns
   // col * kLaneCols .. + kLaneCols.
