@@ -12,17 +12,19 @@
 // its waves and is bound by HBM. A prefill chunk has thousands of rows per KV head, and every
 // K/V tile serves all of them: the work is MFMA-bound. Here every wave owns 16 rows with the full
 // head dim, all waves of a workgroup share one 32-key K/V tile staged in LDS, and no scores cross
-// waves. At head_dim 512 a workgroup has 8 waves (128 rows): the double-buffered tiles take
-// 131 KB of LDS, so one workgroup fills a CU, and its 8 waves put two on each SIMD (256
-// registers each), so one wave's softmax and LDS traffic run under the other's MFMAs. At head_dim
-// 256 a workgroup has 4 waves (64 rows) and two fit on a CU.
+// waves. At head_dim 512, for chunks of at least 128 rows per KV head, a workgroup has 8 waves
+// (128 rows): the double-buffered tiles take 131 KB of LDS, so one workgroup fills a CU, and its
+// 8 waves put two on each SIMD (256 registers each), so one wave's softmax and LDS traffic run
+// under the other's MFMAs. Shorter chunks at head_dim 512 (one wave per SIMD) and all chunks at
+// head_dim 256 (two workgroups per CU) take 4 waves (64 rows).
 //
 //   - K/V tile of the step (32 keys = two 16-key entries of the tile list, each on its own page)
-//     in LDS, double-buffered, one barrier per step. At head_dim 512 the tile goes from memory
-//     straight into LDS (global_load_lds_dwordx4, one key row of 1 KB per wave instruction),
-//     issued right after the barrier into the buffer that step has just released, so it has a
-//     whole step to land; no registers hold it. At head_dim 256 it is fetched into registers and
-//     written to the other buffer at the end of the next step. K rows are padded by 16 bytes and
+//     in LDS, double-buffered, one barrier per step. In 128-row workgroups the tile goes from
+//     memory straight into LDS (global_load_lds_dwordx4, one key row of 1 KB per wave
+//     instruction), issued right after the barrier into the buffer that step has just released,
+//     so it has a whole step to land; no registers hold it. 64-row workgroups fetch it into
+//     registers and write it to the other buffer one step later (at head_dim 512 around the score
+//     MFMAs, at 256 at the end of the step). K rows are padded by 16 bytes and
 //     their 16-byte chunks XOR-swizzled within 64-byte groups, so the score operand reads (16
 //     keys, same column) are free of bank conflicts; V rows (own buffer) are padded by 32 bytes.
 //   - scores: S^T[32 keys][16 rows] per wave with v_mfma_f32_16x16x32_bf16, A = K (keys x 32
