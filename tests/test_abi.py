@@ -72,7 +72,7 @@ def expected_workspace(B, Hq, ns, D, L=1):
     (dict(batch=1, max_pages_per_seq=8256, num_pages=16384, max_ctx_len=132096), 128),
     (dict(batch=2, max_pages_per_seq=4160, num_pages=16384, max_ctx_len=66560), 64),
     (dict(batch=8, max_pages_per_seq=80, max_ctx_len=1280), 16),      # 16 pairs
-    (dict(num_kv_heads=8, head_dim=256, window=1024), 16),            # 65 tiles, 32 pairs
+    (dict(num_kv_heads=8, head_dim=256, window=1024), 8),             # 32 pairs: key split, 1/CU
     (dict(num_kv_heads=8, head_dim=256, window=1024, sink=4), 16),    # + 1 sink tile
     (dict(batch=32, num_kv_heads=8, head_dim=256, window=1024), 1),   # 256 pairs: key split
     (dict(batch=32, num_kv_heads=8, head_dim=256, window=1024, values_are_keys=1), 2),
@@ -91,7 +91,7 @@ def expected_workspace(B, Hq, ns, D, L=1):
     (dict(batch=1, q_len=64, max_ctx_len=4096), 32),                  # 4 blocks of 128 rows
     (dict(batch=1, num_kv_heads=8, head_dim=256, window=1024, q_len=256), 8),  # 8 x 8 blocks
     (dict(num_q_heads=8, num_kv_heads=1), 64),                        # TP2 share of 4 x 33792
-    (dict(num_q_heads=8, num_kv_heads=4, head_dim=256, window=1024), 32),  # its sliding layer
+    (dict(num_q_heads=8, num_kv_heads=4, head_dim=256, window=1024), 16),  # its sliding layer
     (dict(batch=1, num_q_heads=8, num_kv_heads=1, max_pages_per_seq=8256, num_pages=16384,
           max_ctx_len=132096), 256),                                  # TP2 share of 1 x 132096
 ])
