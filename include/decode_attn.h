@@ -145,11 +145,14 @@ typedef struct {
  * + ceil(sink / 16) for its sink keys) tiles of 16 keys for the longest range one query block
  * walks, e = min(max_ctx_len, W + min(L, Q) - 1 or unlimited), with Q the queries of a block,
  * pairs = batch * Hkv * ceil(L / Q) and target = num_cus workgroups for head_dim 512 with
- * separate pools and G * L <= 16 (2 * num_cus for head_dim 256, when values are keys, or for
- * blocks of 32 rows),
+ * separate pools and G * L <= 16, and for head_dim 512 when G * L >= 64 (2 * num_cus for head_dim
+ * 256, when values are keys, or for blocks of 32 rows),
  *     num_splits = clamp(ceil(target / pairs), 1, min(max_splits, T))
  * so every chunk holds at least one tile when the context allows it (short contexts are
- * latency-bound: more, shorter chunks finish sooner).
+ * latency-bound: more, shorter chunks finish sooner). Single-token layers at head_dim 256 with
+ * G <= 4, separate pools and no sink keys instead take num_splits = clamp(floor(num_cus / pairs),
+ * 1, min(max_splits, T)): one workgroup per CU, each of whose waves walks its own tiles.
+ * force_splits > 0 overrides the rule.
  * Returns DECODE_ATTN_OK, DECODE_ATTN_ERR_NULL, _SHAPE, _UNSUPPORTED or _HIP (device query).
  */
 int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* plan);
@@ -184,8 +187,9 @@ int decode_attn_sliding(const decode_attn_plan_t* plan, const void* q, const voi
  * Writes the workspace, which holds two planes:
  *     o_part [B, L, Hq, num_splits, D] fp32 at byte offset 0
  *     lse    [B, L, Hq, num_splits]    fp32 at byte offset plan->partial_lse_offset
- * The queries of a sequence are taken in blocks of 16 / G, 32 / G when G * L > 16, or 64 / G
- * when G * L >= 64 (one block when L = 1). Split s of a
+ * The queries of a sequence are taken in blocks of 16 / G, 32 / G when G * L > 16, 64 / G
+ * when G * L >= 64, or 128 / G at head_dim 512 when G * L >= 128 (one block when L = 1).
+ * Split s of a
  * block covers the tiles [floor(s*T/ns), floor((s+1)*T/ns)) of the block's list of T 16-key
  * tiles (ns = num_splits). With lo and n those of the block's first and last query respectively,
  * the list holds the tiles 0 .. ceil(k/16) - 1 that overlap the sink keys [0, k), k = min(sink,
