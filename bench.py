@@ -14,7 +14,7 @@ Steps rotate over copies of the KV pools so that no step finds its K/V in the L2
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --copy-calibration     # plain 1 GiB device copy, for counter scaling
-    python bench.py --copy-rate            # copy bandwidth of hand-written copy kernels
+    python bench.py --copy-rate            # copy and read bandwidth of hand-written kernels
 """
 from __future__ import annotations
 
@@ -186,8 +186,10 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--copy-rate", action="store_true",
                     help="run the copy-rate program (1 GiB device copies by hand-written kernels "
-                         "with and without non-temporal loads/stores, and the runtime's copy): "
-                         "the ceiling of a kernel that reads each byte once and writes it once")
+                         "with and without non-temporal loads/stores, and the runtime's copy; "
+                         "1 GiB read-only passes, one-pass grids and streams of 1-4 workgroups "
+                         "per CU): the ceilings of a kernel that reads each byte once and writes "
+                         "it once, and of one that only streams its inputs")
     ap.add_argument("--k-eq-v", action="store_true",
                     help="layers whose values are their keys: one pool passed as both K and V")
     ap.add_argument("--q-len", type=int, default=1,

@@ -83,7 +83,7 @@ COPY_RATE = os.path.join(HERE, "copy_rate")
 
 def build_copy_rate() -> str:
     """Compile the standalone copy-rate program (``csrc/copy_rate.hip``, not part of the library):
-    the copy bandwidth the part reaches, which ``bench.py --copy-rate`` reports."""
+    the copy and read-only bandwidth the part reaches, which ``bench.py --copy-rate`` reports."""
     tmp = COPY_RATE + ".tmp%d" % os.getpid()
     cmd = ([_hipcc(), "-x", "hip"] + [f for f in COMMON_FLAGS if f != "-fPIC"] +
            [os.path.join(CSRC, "copy_rate.hip"), "-o", tmp])
