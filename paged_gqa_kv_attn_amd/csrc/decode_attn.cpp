@@ -11,8 +11,9 @@
 
 #include "internal.h"
 
-// Single-token decode at head_dim 256 with G <= 4 and one split runs on the key-split stage-1
-// kernel (stage1_ks.hip); 0 keeps it on the column-split kernel of stage1.hip (for A/B builds).
+// Single-token decode at head_dim 256 with G <= 4 and separate pools runs on the key-split
+// stage-1 kernel (stage1_ks.hip); 0 keeps it on the column-split kernel of stage1.hip (for A/B
+// builds).
 #ifndef DECODE_ATTN_KEYSPLIT
 #define DECODE_ATTN_KEYSPLIT 1
 #endif
@@ -23,6 +24,12 @@
 
 namespace decode_attn {
 namespace {
+
+// A layer the key-split stage-1 kernel serves (whole tiles per wave, one merge per workgroup).
+bool keysplit_layer(int head_dim, int group_size, int q_len, int sink, bool shared) {
+  return DECODE_ATTN_KEYSPLIT &&
+         stage1_keysplit_supported(head_dim, group_size, q_len, sink, shared);
+}
 
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
@@ -159,12 +166,10 @@ int run_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool
   hipError_t err;
   if (stage1_use_prefill(plan->group_size, a.q_len))
     err = launch_prefill(a, p.head_dim, plan->group_size, batch, stream);
-  else if (DECODE_ATTN_KEYSPLIT &&
-           (plan->num_splits == 1 ||
+  else if ((plan->num_splits == 1 ||
             (DECODE_ATTN_KS_SPLITS && (int64_t)plan->num_splits * p.batch * p.num_kv_heads <=
                                           (p.num_cus > 0 ? p.num_cus : 256))) &&
-           stage1_keysplit_supported(p.head_dim, plan->group_size, a.q_len, a.sink,
-                                     k_pool == v_pool))
+           keysplit_layer(p.head_dim, plan->group_size, a.q_len, a.sink, k_pool == v_pool))
     err = launch_stage1_keysplit(a, plan->group_size, batch, stream);
   else
     err = launch_stage1(a, p.head_dim, plan->group_size, batch, stream);
@@ -280,17 +285,15 @@ int decode_attn_plan(const decode_attn_problem* problem, decode_attn_plan_t* pla
   // whose 8-wave workgroups keep eight tiles in flight: once the pairs alone give every CU a
   // workgroup, one split (and no merge) beats two (measured on 32 x 8000 keys, 8 KV heads,
   // window 1024: 42.5 against 47.1 us).
-  if (DECODE_ATTN_KEYSPLIT && pairs >= p.num_cus &&
-      stage1_keysplit_supported(p.head_dim, G, p.q_len, p.window > 0 ? p.sink : 0,
-                                p.values_are_keys != 0))
+  const bool ks_layer = keysplit_layer(p.head_dim, G, p.q_len, p.window > 0 ? p.sink : 0,
+                                       p.values_are_keys != 0);
+  if (ks_layer && pairs >= p.num_cus)
     splits = 1;
   // With fewer pairs it also runs such layers, at one workgroup per CU (its 8 waves take two per
   // SIMD): measured on the long_ctx sliding layer (32 pairs) equal to the column-split kernel's
   // two per CU with the caches flushed before each call, 11% faster back to back (12.0 against
   // 13.5 us), and the same on 64 and 16 pairs.
-  else if (DECODE_ATTN_KS_SPLITS &&
-           stage1_keysplit_supported(p.head_dim, G, p.q_len, p.window > 0 ? p.sink : 0,
-                                     p.values_are_keys != 0))
+  else if (DECODE_ATTN_KS_SPLITS && ks_layer)
     splits = p.num_cus / pairs > 1 ? p.num_cus / pairs : 1;
   int64_t cap = (tiles + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
   if (cap > p.max_splits) cap = p.max_splits;
