@@ -17,6 +17,11 @@
 #ifndef DECODE_ATTN_KEYSPLIT
 #define DECODE_ATTN_KEYSPLIT 1
 #endif
+// Stage-1 kernels may fetch the first tile of the chunk the plan's max_ctx_len gives while the
+// sequence's length is in flight (kept when the length gives the same chunk); 0 disables it.
+#ifndef DECODE_ATTN_SPEC
+#define DECODE_ATTN_SPEC 1
+#endif
 // ... and, with several splits, when they give at most one key-split workgroup per CU.
 #ifndef DECODE_ATTN_KS_SPLITS
 #define DECODE_ATTN_KS_SPLITS 1
@@ -163,6 +168,7 @@ int run_stage1(const decode_attn_plan_t* plan, const void* q, const void* k_pool
   a.num_qblocks = qblocks_of(p, plan->group_size);
   a.num_splits = plan->num_splits;
   a.scale_log2 = scale * 1.442695040888963407360f;
+  a.spec_ctx = DECODE_ATTN_SPEC ? p.max_ctx_len : 0;
   hipError_t err;
   if (stage1_use_prefill(plan->group_size, a.q_len))
     err = launch_prefill(a, p.head_dim, plan->group_size, batch, stream);

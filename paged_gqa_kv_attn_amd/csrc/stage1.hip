@@ -29,7 +29,11 @@
 //   * loads run one step ahead in registers: the K registers are refilled for the next step right
 //     after the park (or the score MFMAs), the V registers right after the P.V MFMAs; the page ids
 //     of the step after that are fetched as a small vector (lane u holds tile u's id) one step
-//     earlier still, so no dependent block-table read sits on the critical path.
+//     earlier still, so no dependent block-table read sits on the critical path;
+//   * start (one query token, no sinks): the first tile of the chunk the plan's expected length
+//     gives is fetched while the sequence's length is still in flight, and kept when the length
+//     gives the same chunk, so the length, page-id and tile reads cost two memory round trips
+//     before the first step instead of three.
 // The per-row softmax state is identical in all waves, so no merge is needed at the end: each
 // wave writes its own columns of the partial output.
 
@@ -169,53 +173,6 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
     return ((size_t)b * L + row_query(r)) * a.num_q_heads + (size_t)kvh * G + r % G;
   };
 
-  // Keys of this sequence: [0, sk) (sink keys not inside the window) and [lo, n). They are walked
-  // as a list of T tiles, list index v: the sink tiles 0 .. st-1 first, then the window's tiles
-  // from physical tile w0 = max(st, lo / 16) on, i.e. physical tile v + (v >= st ? shift : 0).
-  // This split takes list entries [t_begin, t_end).
-  //
-  // Query i of the sequence sits at position n - L + i and attends keys t < n_i = n - L + i + 1,
-  // t >= lo_i (its window), or t < sink. The workgroup walks the union over its queries: the
-  // window of its first query up to n_i of its last one.
-  const int max_keys = a.max_pages_per_seq * S;
-  int n_ctx = load_uniform(a.ctx_lens, b);
-  n_ctx = n_ctx < 0 ? 0 : (n_ctx > max_keys ? max_keys : n_ctx);
-  auto query_end = [&](int i) { const int e = n_ctx - L + i + 1; return e < 0 ? 0 : e; };
-  auto window_lo = [&](int e) { return (a.window > 0 && e > a.window) ? e - a.window : 0; };
-  const int q_last = (qb + 1) * kQB < L ? (qb + 1) * kQB - 1 : L - 1;
-  const int n = query_end(q_last);
-  const int lo = window_lo(query_end(qb * kQB));
-  const int sk = sink < lo ? sink : lo;
-  // This lane's rows (scores and softmax use row 16 * rg + col in row group rg).
-  int row_n[RG], row_lo[RG];
-#pragma unroll
-  for (int rg = 0; rg < RG; ++rg) {
-    const int rr = 16 * rg + col;
-    row_n[rg] = GENERAL ? (row_valid(rr) ? query_end(row_query(rr)) : 0) : n;
-    row_lo[rg] = GENERAL ? window_lo(row_n[rg]) : lo;
-  }
-  const int st = (sk + kTile - 1) / kTile;
-  const int w0 = st > lo / kTile ? st : lo / kTile;
-  const int tile_hi = (n + kTile - 1) / kTile;
-  const int T = st + (tile_hi > w0 ? tile_hi - w0 : 0);
-  const int shift = w0 - st;
-  const int t_begin = (int)(((int64_t)split * T) / ns);
-  const int t_end = (int)(((int64_t)(split + 1) * T) / ns);
-  const int tiles_per_page = S / kTile;
-  auto phys_tile = [&](int v) { return (!GENERAL || v >= st) ? v + shift : v; };
-  const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
-
-  if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
-    for (int idx = lane; idx < 16 * RG * kCols; idx += 64) {
-      const int r = idx / kCols;
-      if (row_valid(r)) a.o_part[(out_row(r) * ns + split) * D + c0 + (idx - r * kCols)] = 0.f;
-    }
-    if (wave == 0 && lane < 16 * RG && row_valid(lane))
-      a.lse_part[out_row(lane) * ns + split] = -INFINITY;
-    return;
-  }
-  const int t_last = t_end - 1;
-
   // q block, B operand of the score MFMA of row group rg: row 16 * rg + col, columns
   // c0 + 32*j + 8*grp .. +8; zero for rows past the last query. Every lane loads (a clamped row)
   // so no load sits under a divergent branch.
@@ -244,6 +201,112 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
   const int k_step = KROW ? kRPI * D : 32;  // element offset between the kKSteps loads
   const int v_off = (4 * grp) * D + c0 + kVE * col;
 
+  // Speculative start (one query token, no sinks): the chunk this split would have at the plan's
+  // expected length (a.spec_ctx) gets its page ids and first tile fetched while ctx_lens is still
+  // in flight; they are kept when the actual length gives the same chunk (both fetches then land
+  // one memory round trip earlier) and fetched again otherwise.
+  StepRegs<D, RG, SUB> r;
+  size_t base[SUB];
+  bool ok[SUB];
+  int32_t pid_next = 0;
+  const int tiles_per_page = S / kTile;
+  const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
+  // Base of list entry ti of a chunk [.., t_end_) whose list entry v is physical tile v + shift_
+  // (entries past the chunk re-read its last), with page id phys; ok_ = inside and a valid page.
+  auto geo_base = [&](int ti, int t_end_, int shift_, int phys, bool& ok_) -> size_t {
+    const int tc = (ti < t_end_ ? ti : t_end_ - 1) + shift_;
+    const bool page_ok = (unsigned)phys < (unsigned)a.num_pages;
+    ok_ = ti < t_end_ && page_ok;
+    const int pg = page_ok ? phys : 0;
+    const int within = tc - (tc / tiles_per_page) * tiles_per_page;
+    return (((size_t)pg * a.num_kv_heads + kvh) * S + within * kTile) * D;
+  };
+  auto load_first = [&]() {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int j = 0; j < kKSteps; ++j)
+        r.k[u][j] = load_kv<bf16x8, STREAM>(a.k_pool + base[u] + k_off + k_step * j);
+    if constexpr (!SHARED) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          r.v[u][i] = load_kv<VRow, STREAM>(a.v_pool + base[u] + v_off + i * D);
+    }
+  };
+  const int max_keys = a.max_pages_per_seq * S;
+  int n_ctx = load_uniform(a.ctx_lens, b);
+  int s_begin = 0, s_end = 0, s_shift = 0;
+  bool spec = false;
+  if constexpr (!GENERAL) {
+    const int n_s = a.spec_ctx < max_keys ? a.spec_ctx : max_keys;
+    const int lo_s = (a.window > 0 && n_s > a.window) ? n_s - a.window : 0;
+    s_shift = lo_s / kTile;
+    const int hi_s = (n_s + kTile - 1) / kTile;
+    const int T_s = hi_s > s_shift ? hi_s - s_shift : 0;
+    s_begin = (int)(((int64_t)split * T_s) / ns);
+    s_end = (int)(((int64_t)(split + 1) * T_s) / ns);
+    spec = n_s > 0 && s_begin < s_end;
+    if (spec) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const int tc = (s_begin + u < s_end ? s_begin + u : s_end - 1) + s_shift;
+        base[u] = geo_base(s_begin + u, s_end, s_shift,
+                           load_uniform(table_row, tc / tiles_per_page), ok[u]);
+      }
+      const int tn = (s_begin + SUB + lane % SUB < s_end ? s_begin + SUB + lane % SUB : s_end - 1) +
+                     s_shift;
+      pid_next = table_row[tn / tiles_per_page];
+      load_first();
+    }
+  }
+  __asm__ volatile("; stage-1 speculative loads issued" ::: "memory");
+
+  // Keys of this sequence: [0, sk) (sink keys not inside the window) and [lo, n). They are walked
+  // as a list of T tiles, list index v: the sink tiles 0 .. st-1 first, then the window's tiles
+  // from physical tile w0 = max(st, lo / 16) on, i.e. physical tile v + (v >= st ? shift : 0).
+  // This split takes list entries [t_begin, t_end).
+  //
+  // Query i of the sequence sits at position n - L + i and attends keys t < n_i = n - L + i + 1,
+  // t >= lo_i (its window), or t < sink. The workgroup walks the union over its queries: the
+  // window of its first query up to n_i of its last one.
+  n_ctx = n_ctx < 0 ? 0 : (n_ctx > max_keys ? max_keys : n_ctx);
+  auto query_end = [&](int i) { const int e = n_ctx - L + i + 1; return e < 0 ? 0 : e; };
+  auto window_lo = [&](int e) { return (a.window > 0 && e > a.window) ? e - a.window : 0; };
+  const int q_last = (qb + 1) * kQB < L ? (qb + 1) * kQB - 1 : L - 1;
+  const int n = query_end(q_last);
+  const int lo = window_lo(query_end(qb * kQB));
+  const int sk = sink < lo ? sink : lo;
+  // This lane's rows (scores and softmax use row 16 * rg + col in row group rg).
+  int row_n[RG], row_lo[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg) {
+    const int rr = 16 * rg + col;
+    row_n[rg] = GENERAL ? (row_valid(rr) ? query_end(row_query(rr)) : 0) : n;
+    row_lo[rg] = GENERAL ? window_lo(row_n[rg]) : lo;
+  }
+  const int st = (sk + kTile - 1) / kTile;
+  const int w0 = st > lo / kTile ? st : lo / kTile;
+  const int tile_hi = (n + kTile - 1) / kTile;
+  const int T = st + (tile_hi > w0 ? tile_hi - w0 : 0);
+  const int shift = w0 - st;
+  const int t_begin = (int)(((int64_t)split * T) / ns);
+  const int t_end = (int)(((int64_t)(split + 1) * T) / ns);
+  auto phys_tile = [&](int v) { return (!GENERAL || v >= st) ? v + shift : v; };
+
+  if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
+    for (int idx = lane; idx < 16 * RG * kCols; idx += 64) {
+      const int r = idx / kCols;
+      if (row_valid(r)) a.o_part[(out_row(r) * ns + split) * D + c0 + (idx - r * kCols)] = 0.f;
+    }
+    if (wave == 0 && lane < 16 * RG && row_valid(lane))
+      a.lse_part[out_row(lane) * ns + split] = -INFINITY;
+    __builtin_amdgcn_s_waitcnt(0);  // speculative loads land before the wave ends
+    return;
+  }
+  const int t_last = t_end - 1;
+
   // Tiles past the split re-read its last tile (an L2 hit; they are masked) so every load is
   // unconditional and the compiler can count outstanding loads exactly. Invalid page ids are
   // never dereferenced: page 0 is read instead and the tile is masked.
@@ -262,26 +325,15 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
     return table_row[tc / tiles_per_page];
   };
 
-  StepRegs<D, RG, SUB> r;
-  size_t base[SUB];
-  bool ok[SUB];
+  const bool hit = spec && shift == s_shift && t_begin == s_begin && t_end == s_end;
+  if (!hit) {
 #pragma unroll
-  for (int u = 0; u < SUB; ++u) {
-    const int tc = phys_tile(clamp_tile(t_begin + u));
-    base[u] = tile_base(t_begin + u, load_uniform(table_row, tc / tiles_per_page), ok[u]);
-  }
-  int32_t pid_next = load_page_ids(t_begin + SUB);
-#pragma unroll
-  for (int u = 0; u < SUB; ++u)
-#pragma unroll
-    for (int j = 0; j < kKSteps; ++j)
-      r.k[u][j] = load_kv<bf16x8, STREAM>(a.k_pool + base[u] + k_off + k_step * j);
-  if constexpr (!SHARED) {
-#pragma unroll
-    for (int u = 0; u < SUB; ++u)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        r.v[u][i] = load_kv<VRow, STREAM>(a.v_pool + base[u] + v_off + i * D);
+    for (int u = 0; u < SUB; ++u) {
+      const int tc = phys_tile(clamp_tile(t_begin + u));
+      base[u] = tile_base(t_begin + u, load_uniform(table_row, tc / tiles_per_page), ok[u]);
+    }
+    pid_next = load_page_ids(t_begin + SUB);
+    load_first();
   }
   // A fence the loop latch does not have: otherwise the identical trailing V loads of this
   // prologue and of the loop body get merged into the loop header, which would turn the V

@@ -11,7 +11,9 @@
 // score exchange and no per-tile barrier. The waves' softmax states are merged once, through LDS,
 // when the chunk is done. A tile of one (page, kv head) is 16 x 256 bf16 = 8 KB contiguous; each
 // wave keeps one tile of K and V in flight while it computes the previous one, so a workgroup has
-// NW tiles in flight (the column-split kernel of stage1.hip has one per workgroup).
+// NW tiles in flight (the column-split kernel of stage1.hip has one per workgroup). As there,
+// the first tiles of the chunk the plan's expected length gives are fetched while the sequence's
+// length is in flight, and kept when the length gives the same chunk.
 //
 //   * K: loaded in row order (load j brings keys 2j, 2j + 1: 1 KB, whole 128-byte lines), parked in
 //     the wave's LDS slice and read back in the A layout of v_mfma_f32_16x16x32_bf16 (lane l: key
@@ -138,25 +140,53 @@ __global__ __launch_bounds__(64 * NW) void stage1_ks_kernel(const Stage1Args a) 
   const int max_keys = a.max_pages_per_seq * S;
   const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
 
-  int n_ctx = load_uniform(a.ctx_lens, b);
-  n_ctx = n_ctx < 0 ? 0 : (n_ctx > max_keys ? max_keys : n_ctx);
-  const KsRange R = ks_range(n_ctx, a.window);
-  const int t_begin = (int)(((int64_t)split * R.T) / ns);
-  const int t_end = (int)(((int64_t)(split + 1) * R.T) / ns);
-  const size_t out_row0 = (size_t)b * a.num_q_heads + (size_t)kvh * G;
+  // Element offsets inside a tile. K in row order: load j brings keys 2j + lane / 32, dims
+  // 8 (lane % 32). V: MFMA, load 2i + h brings key 4grp + i, dims 8col + 128h; VALU, row order
+  // as K.
+  const int k_off = 8 * lane;
+  const int v_off = kValu ? 8 * lane : 4 * grp * D + 8 * col;
+  auto v_elem = [&](int j) { return kValu ? 512 * j : (j >> 1) * D + 128 * (j & 1); };
+  // Base of tile entry t (clamped to the chunk's last, t_end - 1) of the chunk whose tiles start
+  // at physical tile w0, with its page id phys; ok = the id is a valid page.
+  auto entry_base = [&](int w0, int t, int t_end_, int phys, bool& ok_) -> size_t {
+    const int tc = t < t_end_ ? t : t_end_ - 1;
+    const bool page_ok = (unsigned)phys < (unsigned)a.num_pages;
+    ok_ = page_ok;
+    const int pt = w0 + tc;
+    const int within = pt - (pt / tiles_per_page) * tiles_per_page;
+    return (((size_t)(page_ok ? phys : 0) * a.num_kv_heads + kvh) * S + within * kTile) * D;
+  };
+  u32x4 kr[8], vr[8];
+  auto load_tile = [&](size_t base_) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      kr[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(a.k_pool + base_ + k_off + 512 * j));
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      vr[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(a.v_pool + base_ + v_off + v_elem(j)));
+  };
 
-  if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
-    for (int idx = tid; idx < G * D; idx += kKsThreads)
-      a.o_part[((out_row0 + idx / D) * ns + split) * D + idx % D] = 0.f;
-    if (tid < G) a.lse_part[(out_row0 + tid) * ns + split] = -INFINITY;
-    return;
-  }
-  const int t_last = t_end - 1;
-  const int my_first = t_begin + wave;  // this wave's tiles: my_first + 4s < t_end
-  const int my_count = my_first < t_end ? (t_end - my_first + kKsWaves - 1) / kKsWaves : 0;
+  // Speculative start: the chunk this split would have at the plan's expected length (a.spec_ctx)
+  // gets its page ids and first tile fetched while ctx_lens is still in flight; they are kept
+  // when the actual length gives the same chunk (then both fetches are one memory round trip
+  // earlier), and fetched again otherwise.
+  int n_ctx = load_uniform(a.ctx_lens, b);
+  const int n_spec = a.spec_ctx < max_keys ? a.spec_ctx : max_keys;
+  const KsRange Rs = ks_range(n_spec, a.window);
+  const int ts_begin = (int)(((int64_t)split * Rs.T) / ns);
+  const int ts_end = (int)(((int64_t)(split + 1) * Rs.T) / ns);
+  const bool spec = n_spec > 0 && ts_begin < ts_end;
   int32_t pid_vec = 0;
-  if (my_count > 0)
-    pid_vec = ks_page_ids<NW>(table_row, R.w0, my_first, t_last, tiles_per_page, lane);
+  bool ok = false;
+  size_t base = 0;
+  if (spec) {
+    pid_vec = ks_page_ids<NW>(table_row, Rs.w0, ts_begin + wave, ts_end - 1, tiles_per_page, lane);
+    base = entry_base(Rs.w0, ts_begin + wave, ts_end, __builtin_amdgcn_readlane(pid_vec, 0), ok);
+    load_tile(base);
+  }
+  const size_t out_row0 = (size_t)b * a.num_q_heads + (size_t)kvh * G;
 
   // q of the group. MFMA: the B operand, column col is head kvh * G + col (zero for col >= G),
   // dims 32k + 8grp. VALU: every lane holds dims 8 (lane % 32) .. + 8 of each head, as bf16 pairs.
@@ -174,6 +204,29 @@ __global__ __launch_bounds__(64 * NW) void stage1_ks_kernel(const Stage1Args a) 
       const u32x4 z = {0u, 0u, 0u, 0u};
       qop[k] = __builtin_bit_cast(bf16x8, col < G ? v : z);
     }
+  }
+  __asm__ volatile("; ks speculative loads issued" ::: "memory");
+
+  n_ctx = n_ctx < 0 ? 0 : (n_ctx > max_keys ? max_keys : n_ctx);
+  const KsRange R = ks_range(n_ctx, a.window);
+  const int t_begin = (int)(((int64_t)split * R.T) / ns);
+  const int t_end = (int)(((int64_t)(split + 1) * R.T) / ns);
+
+  if (t_begin >= t_end) {  // empty split: o = 0, lse = -inf
+    for (int idx = tid; idx < G * D; idx += kKsThreads)
+      a.o_part[((out_row0 + idx / D) * ns + split) * D + idx % D] = 0.f;
+    if (tid < G) a.lse_part[(out_row0 + tid) * ns + split] = -INFINITY;
+    __builtin_amdgcn_s_waitcnt(0);  // speculative loads land before the wave ends
+    return;
+  }
+  const int t_last = t_end - 1;
+  const int my_first = t_begin + wave;  // this wave's tiles: my_first + NW s < t_end
+  const int my_count = my_first < t_end ? (t_end - my_first + kKsWaves - 1) / kKsWaves : 0;
+  const bool hit = spec && Rs.w0 == R.w0 && ts_begin == t_begin && ts_end == t_end;
+  if (!hit && my_count > 0) {
+    pid_vec = ks_page_ids<NW>(table_row, R.w0, my_first, t_last, tiles_per_page, lane);
+    base = entry_base(R.w0, my_first, t_end, __builtin_amdgcn_readlane(pid_vec, 0), ok);
+    load_tile(base);
   }
 
   // MFMA: m_run / l_run of head col; acc[e][i]: head 4grp + i, dim 8col + e % 8 + 128 (e / 8).
@@ -195,33 +248,10 @@ __global__ __launch_bounds__(64 * NW) void stage1_ks_kernel(const Stage1Args a) 
     for (int e = 0; e < 8; ++e) ov[h][e] = 0.f;
 
   if (my_count > 0) {
-    // Element offsets inside a tile. K in row order: load j brings keys 2j + lane / 32, dims
-    // 8 (lane % 32). V: MFMA, load 2i + h brings key 4grp + i, dims 8col + 128h; VALU, row order
-    // as K.
-    const int k_off = 8 * lane;
-    const int v_off = kValu ? 8 * lane : 4 * grp * D + 8 * col;
-    auto v_elem = [&](int j) { return kValu ? 512 * j : (j >> 1) * D + 128 * (j & 1); };
-    auto tile_base = [&](int s, bool& ok) -> size_t {
-      const int t = my_first + kKsWaves * s;
-      const int tc = t < t_end ? t : t_last;
-      const int phys = __builtin_amdgcn_readlane(pid_vec, s & 63);
-      const bool page_ok = (unsigned)phys < (unsigned)a.num_pages;
-      ok = page_ok;
-      const int pt = R.w0 + tc;
-      const int within = pt - (pt / tiles_per_page) * tiles_per_page;
-      return (((size_t)(page_ok ? phys : 0) * a.num_kv_heads + kvh) * S + within * kTile) * D;
+    auto tile_base = [&](int s, bool& ok_) -> size_t {
+      return entry_base(R.w0, my_first + kKsWaves * s, t_end,
+                        __builtin_amdgcn_readlane(pid_vec, s & 63), ok_);
     };
-    bool ok;
-    size_t base = tile_base(0, ok);
-    u32x4 kr[8], vr[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      kr[j] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(a.k_pool + base + k_off + 512 * j));
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      vr[j] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(a.v_pool + base + v_off + v_elem(j)));
     __asm__ volatile("; ks prologue loads issued" ::: "memory");
 
     for (int s = 0; s < my_count; ++s) {
