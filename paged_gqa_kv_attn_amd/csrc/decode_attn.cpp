@@ -17,7 +17,7 @@
 #ifndef DECODE_ATTN_KEYSPLIT
 #define DECODE_ATTN_KEYSPLIT 1
 #endif
-// Stage-1 kernels may fetch the first tile of the chunk the plan's max_ctx_len gives while the
+// Stage-1 kernels may fetch the page ids of the chunk the plan's max_ctx_len gives while the
 // sequence's length is in flight (kept when the length gives the same chunk); 0 disables it.
 #ifndef DECODE_ATTN_SPEC
 #define DECODE_ATTN_SPEC 1

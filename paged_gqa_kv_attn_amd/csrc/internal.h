@@ -37,7 +37,7 @@ struct Stage1Args {
   int32_t num_splits;
   float scale_log2;             // scale * log2(e): scores in base-2 units
   int32_t spec_ctx;             // the plan's expected context length (0 = none): a kernel may
-                                // fetch the first tile of that length's chunk before ctx_lens
+                                // fetch the page ids of that length's chunk before ctx_lens
 };
 
 // Kernel arguments of stage 2 (one workgroup per (64-wide slice of D, q head, sequence)).

@@ -30,8 +30,8 @@
 //     after the park (or the score MFMAs), the V registers right after the P.V MFMAs; the page ids
 //     of the step after that are fetched as a small vector (lane u holds tile u's id) one step
 //     earlier still, so no dependent block-table read sits on the critical path;
-//   * start (one query token, no sinks): the first tile of the chunk the plan's expected length
-//     gives is fetched while the sequence's length is still in flight, and kept when the length
+//   * start (one query token, no sinks): the page ids of the chunk the plan's expected length
+//     gives are fetched while the sequence's length is still in flight, and kept when the length
 //     gives the same chunk, so the length, page-id and tile reads cost two memory round trips
 //     before the first step instead of three.
 // The per-row softmax state is identical in all waves, so no merge is needed at the end: each
@@ -201,40 +201,17 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
   const int k_step = KROW ? kRPI * D : 32;  // element offset between the kKSteps loads
   const int v_off = (4 * grp) * D + c0 + kVE * col;
 
-  // Speculative start (one query token, no sinks): the chunk this split would have at the plan's
-  // expected length (a.spec_ctx) gets its page ids and first tile fetched while ctx_lens is still
-  // in flight; they are kept when the actual length gives the same chunk (both fetches then land
-  // one memory round trip earlier) and fetched again otherwise.
+  // Speculative start (one query token, no sinks): the page ids of the chunk this split would have
+  // at the plan's expected length (a.spec_ctx) are fetched while ctx_lens is still in flight, and
+  // kept when the actual length gives the same chunk (the first tiles' fetch then leaves one
+  // memory round trip earlier); otherwise they are fetched again.
   StepRegs<D, RG, SUB> r;
   size_t base[SUB];
   bool ok[SUB];
+  int32_t pid_first[SUB];  // page ids of list entries t_begin .. t_begin + SUB - 1
   int32_t pid_next = 0;
   const int tiles_per_page = S / kTile;
   const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
-  // Base of list entry ti of a chunk [.., t_end_) whose list entry v is physical tile v + shift_
-  // (entries past the chunk re-read its last), with page id phys; ok_ = inside and a valid page.
-  auto geo_base = [&](int ti, int t_end_, int shift_, int phys, bool& ok_) -> size_t {
-    const int tc = (ti < t_end_ ? ti : t_end_ - 1) + shift_;
-    const bool page_ok = (unsigned)phys < (unsigned)a.num_pages;
-    ok_ = ti < t_end_ && page_ok;
-    const int pg = page_ok ? phys : 0;
-    const int within = tc - (tc / tiles_per_page) * tiles_per_page;
-    return (((size_t)pg * a.num_kv_heads + kvh) * S + within * kTile) * D;
-  };
-  auto load_first = [&]() {
-#pragma unroll
-    for (int u = 0; u < SUB; ++u)
-#pragma unroll
-      for (int j = 0; j < kKSteps; ++j)
-        r.k[u][j] = load_kv<bf16x8, STREAM>(a.k_pool + base[u] + k_off + k_step * j);
-    if constexpr (!SHARED) {
-#pragma unroll
-      for (int u = 0; u < SUB; ++u)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          r.v[u][i] = load_kv<VRow, STREAM>(a.v_pool + base[u] + v_off + i * D);
-    }
-  };
   const int max_keys = a.max_pages_per_seq * S;
   int n_ctx = load_uniform(a.ctx_lens, b);
   int s_begin = 0, s_end = 0, s_shift = 0;
@@ -252,13 +229,11 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
 #pragma unroll
       for (int u = 0; u < SUB; ++u) {
         const int tc = (s_begin + u < s_end ? s_begin + u : s_end - 1) + s_shift;
-        base[u] = geo_base(s_begin + u, s_end, s_shift,
-                           load_uniform(table_row, tc / tiles_per_page), ok[u]);
+        pid_first[u] = load_uniform(table_row, tc / tiles_per_page);
       }
       const int tn = (s_begin + SUB + lane % SUB < s_end ? s_begin + SUB + lane % SUB : s_end - 1) +
                      s_shift;
       pid_next = table_row[tn / tiles_per_page];
-      load_first();
     }
   }
   __asm__ volatile("; stage-1 speculative loads issued" ::: "memory");
@@ -302,7 +277,7 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
     }
     if (wave == 0 && lane < 16 * RG && row_valid(lane))
       a.lse_part[out_row(lane) * ns + split] = -INFINITY;
-    __builtin_amdgcn_s_waitcnt(0);  // speculative loads land before the wave ends
+    __builtin_amdgcn_s_waitcnt(0);  // the early loads land before the wave ends
     return;
   }
   const int t_last = t_end - 1;
@@ -330,10 +305,23 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       const int tc = phys_tile(clamp_tile(t_begin + u));
-      base[u] = tile_base(t_begin + u, load_uniform(table_row, tc / tiles_per_page), ok[u]);
+      pid_first[u] = load_uniform(table_row, tc / tiles_per_page);
     }
     pid_next = load_page_ids(t_begin + SUB);
-    load_first();
+  }
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) base[u] = tile_base(t_begin + u, pid_first[u], ok[u]);
+#pragma unroll
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int j = 0; j < kKSteps; ++j)
+      r.k[u][j] = load_kv<bf16x8, STREAM>(a.k_pool + base[u] + k_off + k_step * j);
+  if constexpr (!SHARED) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r.v[u][i] = load_kv<VRow, STREAM>(a.v_pool + base[u] + v_off + i * D);
   }
   // A fence the loop latch does not have: otherwise the identical trailing V loads of this
   // prologue and of the loop body get merged into the loop header, which would turn the V

@@ -12,7 +12,7 @@
 // when the chunk is done. A tile of one (page, kv head) is 16 x 256 bf16 = 8 KB contiguous; each
 // wave keeps one tile of K and V in flight while it computes the previous one, so a workgroup has
 // NW tiles in flight (the column-split kernel of stage1.hip has one per workgroup). As there,
-// the first tiles of the chunk the plan's expected length gives are fetched while the sequence's
+// the page ids of the chunk the plan's expected length gives are fetched while the sequence's
 // length is in flight, and kept when the length gives the same chunk.
 //
 //   * K: loaded in row order (load j brings keys 2j, 2j + 1: 1 KB, whole 128-byte lines), parked in
@@ -168,26 +168,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_ks_kernel(const Stage1Args a) 
           reinterpret_cast<const u32x4*>(a.v_pool + base_ + v_off + v_elem(j)));
   };
 
-  // Speculative start: the chunk this split would have at the plan's expected length (a.spec_ctx)
-  // gets its page ids and first tile fetched while ctx_lens is still in flight; they are kept
-  // when the actual length gives the same chunk (then both fetches are one memory round trip
-  // earlier), and fetched again otherwise.
-  int n_ctx = load_uniform(a.ctx_lens, b);
-  const int n_spec = a.spec_ctx < max_keys ? a.spec_ctx : max_keys;
-  const KsRange Rs = ks_range(n_spec, a.window);
-  const int ts_begin = (int)(((int64_t)split * Rs.T) / ns);
-  const int ts_end = (int)(((int64_t)(split + 1) * Rs.T) / ns);
-  const bool spec = n_spec > 0 && ts_begin < ts_end;
-  int32_t pid_vec = 0;
-  bool ok = false;
-  size_t base = 0;
-  if (spec) {
-    pid_vec = ks_page_ids<NW>(table_row, Rs.w0, ts_begin + wave, ts_end - 1, tiles_per_page, lane);
-    base = entry_base(Rs.w0, ts_begin + wave, ts_end, __builtin_amdgcn_readlane(pid_vec, 0), ok);
-    load_tile(base);
-  }
   const size_t out_row0 = (size_t)b * a.num_q_heads + (size_t)kvh * G;
-
   // q of the group. MFMA: the B operand, column col is head kvh * G + col (zero for col >= G),
   // dims 32k + 8grp. VALU: every lane holds dims 8 (lane % 32) .. + 8 of each head, as bf16 pairs.
   bf16x8 qop[kValu ? 1 : kKSteps];
@@ -205,6 +186,19 @@ __global__ __launch_bounds__(64 * NW) void stage1_ks_kernel(const Stage1Args a) 
       qop[k] = __builtin_bit_cast(bf16x8, col < G ? v : z);
     }
   }
+  // Speculative start: the page ids of the chunk this split would have at the plan's expected
+  // length (a.spec_ctx) are fetched while ctx_lens is still in flight, and kept when the actual
+  // length gives the same chunk (the first tile's fetch then leaves one memory round trip
+  // earlier); otherwise they are fetched again.
+  int n_ctx = load_uniform(a.ctx_lens, b);
+  const int n_spec = a.spec_ctx < max_keys ? a.spec_ctx : max_keys;
+  const KsRange Rs = ks_range(n_spec, a.window);
+  const int ts_begin = (int)(((int64_t)split * Rs.T) / ns);
+  const int ts_end = (int)(((int64_t)(split + 1) * Rs.T) / ns);
+  const bool spec = n_spec > 0 && ts_begin < ts_end;
+  int32_t pid_vec = 0;
+  if (spec)
+    pid_vec = ks_page_ids<NW>(table_row, Rs.w0, ts_begin + wave, ts_end - 1, tiles_per_page, lane);
   __asm__ volatile("; ks speculative loads issued" ::: "memory");
 
   n_ctx = n_ctx < 0 ? 0 : (n_ctx > max_keys ? max_keys : n_ctx);
@@ -216,15 +210,18 @@ __global__ __launch_bounds__(64 * NW) void stage1_ks_kernel(const Stage1Args a) 
     for (int idx = tid; idx < G * D; idx += kKsThreads)
       a.o_part[((out_row0 + idx / D) * ns + split) * D + idx % D] = 0.f;
     if (tid < G) a.lse_part[(out_row0 + tid) * ns + split] = -INFINITY;
-    __builtin_amdgcn_s_waitcnt(0);  // speculative loads land before the wave ends
+    __builtin_amdgcn_s_waitcnt(0);  // the early loads land before the wave ends
     return;
   }
   const int t_last = t_end - 1;
   const int my_first = t_begin + wave;  // this wave's tiles: my_first + NW s < t_end
   const int my_count = my_first < t_end ? (t_end - my_first + kKsWaves - 1) / kKsWaves : 0;
   const bool hit = spec && Rs.w0 == R.w0 && ts_begin == t_begin && ts_end == t_end;
-  if (!hit && my_count > 0) {
+  if (!hit && my_count > 0)
     pid_vec = ks_page_ids<NW>(table_row, R.w0, my_first, t_last, tiles_per_page, lane);
+  bool ok = false;
+  size_t base = 0;
+  if (my_count > 0) {
     base = entry_base(R.w0, my_first, t_end, __builtin_amdgcn_readlane(pid_vec, 0), ok);
     load_tile(base);
   }
