@@ -9,9 +9,11 @@
 //
 // One pass: one workgroup per (64-wide slice of d, query head, sequence), 256 threads = 16 split
 // groups of 16 threads; a thread owns 4 consecutive d and walks splits g, g+16, ... in batches of
-// kBatch whose loads (partial rows and their lse) are all issued before any is used. Each thread
-// keeps a running max, weight sum and weighted sum (rescaled when the max grows), so no separate
-// pass over the lse values is needed. The 16 group states are merged in LDS in a fixed order
+// B whose loads (partial rows and their lse) are all issued before any is used. B is the smallest
+// power of two up to 8 with 16 B >= num_splits, so a plan with few splits issues no loads past its
+// last split (clamped re-reads measured 0.4 us of a 4.4 us merge at 32 splits). Each thread keeps
+// a running max, weight sum and weighted sum (rescaled when the max grows), so no separate pass
+// over the lse values is needed. The 16 group states are merged in LDS in a fixed order
 // (deterministic).
 
 #include <hip/hip_runtime.h>
@@ -25,10 +27,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGroups = 16;                              // split groups per workgroup
 constexpr int kGroupThreads = kStage2Threads / kGroups;  // 16 threads x 4 d = 64 d
-constexpr int kBatch = 8;                                // splits per thread per round of loads
+#ifndef DECODE_ATTN_STAGE2_BATCH
+#define DECODE_ATTN_STAGE2_BATCH 0
+#endif
 constexpr float kLog2e = 1.442695040888963407360f;
 constexpr float kLn2f = 0.693147180559945309417f;
 
+template <int kBatch>  // splits per thread per round of loads
 __global__ __launch_bounds__(kStage2Threads) void stage2_kernel(const Stage2Args a) {
   __shared__ f32x4 acc_lds[kGroups][kGroupThreads];
   __shared__ float m_lds[kGroups];
@@ -114,8 +119,13 @@ hipError_t launch_stage2(const Stage2Args& args, int batch, hipStream_t stream) 
   dim3 grid(args.head_dim / 64, args.num_q_heads, batch);
   dim3 block(kStage2Threads);
   void* kargs[] = {const_cast<Stage2Args*>(&args)};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&stage2_kernel), grid, block, kargs, 0,
-                         stream);
+  // DECODE_ATTN_STAGE2_BATCH (build knob, for A/B builds): 0 = by the split count, else that batch.
+  const int ns = DECODE_ATTN_STAGE2_BATCH ? DECODE_ATTN_STAGE2_BATCH * kGroups : args.num_splits;
+  const void* fn = ns <= kGroups       ? reinterpret_cast<const void*>(&stage2_kernel<1>)
+                   : ns <= 2 * kGroups ? reinterpret_cast<const void*>(&stage2_kernel<2>)
+                   : ns <= 4 * kGroups ? reinterpret_cast<const void*>(&stage2_kernel<4>)
+                                       : reinterpret_cast<const void*>(&stage2_kernel<8>);
+  return hipLaunchKernel(fn, grid, block, kargs, 0, stream);
 }
 
 }  // namespace decode_attn
