@@ -30,10 +30,12 @@ def _hipcc() -> str:
     return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-# Per-source flags. The prefill kernel keeps its MFMA accumulators in ordinary VGPRs: with the
-# default heuristics the score and output accumulators both claim AGPRs and the compiler moves the
-# output block between the two register files on every loop step.
-SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+# Per-source flags. The prefill and stage-1 kernels keep their MFMA accumulators in ordinary VGPRs:
+# with the default heuristics the output accumulators live in AGPRs for the MFMAs and in VGPRs for
+# the softmax rescale, and the compiler copies the output block between the two register files on
+# every loop step (stage 1: 32 copies per step at head_dim 512, 208 with two row groups).
+SOURCE_FLAGS = {"prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+                "stage1.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, extra=()) -> str:
