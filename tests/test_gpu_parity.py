@@ -72,6 +72,26 @@ def test_forced_split_counts_agree():
         np.testing.assert_allclose(o, outs[0], atol=gu.MAX_ABS, rtol=0)
 
 
+@pytest.mark.parametrize("D,G,window", [(512, 8, 0), (512, 4, 200), (256, 2, 1024), (256, 8, 300)])
+def test_plan_length_other_than_the_contexts(D, G, window):
+    """The plan's max_ctx_len only sizes the split count, and the kernels fetch the first page ids
+    of the chunk it gives before the sequences' lengths arrive: every sequence at that length
+    (kept), none (fetched again), some, a plan length below the contexts and none (0) all give
+    the same results. Covers the column-split kernel (head_dim 512, and head_dim 256 with G = 8)
+    and the key-split kernel (head_dim 256, G = 2)."""
+    print("plan length D=%d G=%d W=%d" % (D, G, window), flush=True)
+    Hkv = 2
+    ctx = [3000, 3000, 2100, 3000]
+    inp = make_layer_inputs(ctx, G * Hkv, Hkv, D, page_size=16, window=window,
+                            seed=[34, D, G, window], q_mult=1.5)
+    ref = gu.reference(inp)
+    t = gu.upload(inp)
+    for max_ctx in (3000, 4096, 2100, 1000, 0):
+        for splits in (0, 5):
+            out, lse = gu.run(inp, dev_bufs=t, max_ctx_len=max_ctx, force_splits=splits)
+            gu.compare(out, lse, *ref, "plan length %d ns%d" % (max_ctx, splits))
+
+
 def test_page_permutation_is_bitwise_invariant():
     inp = make_layer_inputs([900, 333], 8, 1, 512, page_size=16, seed=12)
     out, lse = gu.run(inp)
