@@ -104,8 +104,11 @@ typedef struct {
   int32_t page_size;         /* S: tokens per page, a multiple of 16, 16 <= S <= 1024 */
   int32_t max_pages_per_seq; /* columns (row stride) of the block table, >= 1 */
   int32_t num_pages;         /* P: pages in each pool, >= 1 */
-  int32_t max_ctx_len;       /* longest context expected; sizes the split count only. Longer
-                                contexts are still computed correctly. 0 = max_pages_per_seq * S */
+  int32_t max_ctx_len;       /* longest context expected; sizes the split count, and single-token
+                                calls fetch the first page ids of the chunk a sequence of this length
+                                would have before its actual length arrives (kept when that length
+                                gives the same chunk). Other lengths are still computed correctly.
+                                0 = max_pages_per_seq * S for the split count, no early fetch */
   int32_t window;            /* 0: global layer; W > 0: sliding layer attending the last W keys */
   int32_t num_cus;           /* compute units to plan for; 0 = query the current HIP device */
   int32_t max_splits;        /* cap on num_splits; 0 = library default (256) */
