@@ -24,11 +24,15 @@
 //     instruction), issued right after the barrier into the buffer that step has just released,
 //     so it has a whole step to land; no registers hold it. 64-row workgroups fetch it into
 //     registers and write it to the other buffer one step later (at head_dim 512 around the score
-//     MFMAs, at 256 at the end of the step). K rows are padded by 16 bytes and
-//     their 16-byte chunks XOR-swizzled within 64-byte groups, so the score operand reads (16
-//     keys, same column) are free of bank conflicts; V rows (own buffer) are padded by 32 bytes.
+//     MFMAs, at 256 at the end of the step). K and V rows are padded by 32 bytes: gfx950 serves a
+//     16-byte LDS read in passes that pair lanes i and i + 16, and with a row pitch of 32 bytes
+//     mod 256 the score operand reads (16 keys, same 16-byte column) fill all 64 banks in every
+//     pass (measured: no bank conflicts; a 16-byte pad cost about 4 conflict cycles per read).
 //   - scores: S^T[32 keys][16 rows] per wave with v_mfma_f32_16x16x32_bf16, A = K (keys x 32
-//     columns, from LDS), B = the wave's q rows (in registers for the whole kernel);
+//     columns, from LDS), B = the wave's q rows (in registers for the whole kernel). In 128-row
+//     workgroups the operand reads run 4 ahead of the MFMAs (scheduling barriers keep the
+//     compiler from pulling each read down to its MFMA), and both MFMA phases of a step run at
+//     raised wave priority, so the SIMD's other wave yields its issue slots to them;
 //   - online softmax per row in base 2, exactly as the decode kernel (masks by select, running
 //     max and sum, accumulator rescaled only when a max moved);
 //   - P.V with v_mfma_f32_16x16x32_bf16: A = P (16 rows x 32 keys) straight from the score
@@ -87,6 +91,29 @@ constexpr bool kTr = DECODE_ATTN_PREFILL_TR;
 #define DECODE_ATTN_PREFILL_DMA 1
 #endif
 constexpr bool kDma = DECODE_ATTN_PREFILL_DMA;
+// Score operand reads in flight ahead of the MFMAs (128-row workgroups; 0 = the compiler's order,
+// which reads each operand just before its MFMA); KPIPE_SB: bit 0 pins the order.
+#ifndef DECODE_ATTN_PREFILL_KPIPE
+#define DECODE_ATTN_PREFILL_KPIPE 4
+#endif
+constexpr int kKPipe = DECODE_ATTN_PREFILL_KPIPE;
+constexpr int kKPipeN = kKPipe > 0 ? kKPipe : 1;  // register slots of the score operand reads
+#ifndef DECODE_ATTN_PREFILL_KPIPE_SB
+#define DECODE_ATTN_PREFILL_KPIPE_SB 1
+#endif
+// The direct fetches' LDS addresses carry no alias information (below, dma16).
+#ifndef DECODE_ATTN_PREFILL_DMA_OPAQUE
+#define DECODE_ATTN_PREFILL_DMA_OPAQUE 1
+#endif
+#ifndef DECODE_ATTN_PREFILL_SETPRIO
+#define DECODE_ATTN_PREFILL_SETPRIO 1
+#endif
+// MFMA phases (scores, P.V) at raised wave priority, so that a SIMD's other wave yields to them.
+constexpr bool kSetPrio = DECODE_ATTN_PREFILL_SETPRIO;
+// Padding of a K row in LDS (bf16 elements).
+#ifndef DECODE_ATTN_PREFILL_PAD
+#define DECODE_ATTN_PREFILL_PAD 16
+#endif
 #ifndef DECODE_ATTN_PREFILL_XCD
 #define DECODE_ATTN_PREFILL_XCD 1
 #endif
@@ -95,7 +122,7 @@ constexpr bool kXcdRemap = DECODE_ATTN_PREFILL_XCD;  // query blocks of a KV hea
 template <int D, int ROWS>
 struct PShape {
   static_assert(D == 256 || D == 512, "head_dim");
-  static constexpr int kPitch = D + 8;                      // LDS row pitch, bf16
+  static constexpr int kPitch = D + DECODE_ATTN_PREFILL_PAD;  // LDS row pitch, bf16
   static constexpr int kVPitch = kTr ? D + 16 : D + 8;      // V rows (own buffer), bf16
   static constexpr int kChunks = D / 8;                     // 16-byte chunks per key row
   static constexpr int kQSteps = D / 32;                    // score MFMAs per 16 keys
@@ -119,7 +146,19 @@ __device__ __forceinline__ int swz(int c) {
 // 16 bytes per lane from global memory to LDS: lane l's bytes land at l_base + 16 l (l_base
 // wave-uniform), so one instruction fills 1 KB of LDS, checked lane by lane on gfx950.
 __device__ __forceinline__ void dma16(const uint16_t* g, uint16_t* l_base) {
+#if DECODE_ATTN_PREFILL_DMA_OPAQUE
+  // The LDS address passes through an empty asm statement, so the fetch carries no alias
+  // information about the tile buffers. Otherwise the compiler may find that the first score read
+  // of a step can alias the fetch of the tile two steps ahead (same array, other buffer) and wait
+  // for every fetch in flight before it. The kernel's own waits order the fetches: all land before
+  // the edge masking and the barrier that publishes their buffer.
+  uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(l_base);
+  asm volatile("" : "+s"(l));
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(uintptr_t)l, 16, 0,
+                                   0);
+#else
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)(l_base), 16, 0, 0);
+#endif
 }
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane i gets element (i & 3) of the 4-element
@@ -208,7 +247,17 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
   const int shift = w0 - st;
   const int t_begin = (int)(((int64_t)split * T) / ns);
   const int t_end = (int)(((int64_t)(split + 1) * T) / ns);
-  const int tiles_per_page = S / kTile;
+  // Tile pc lies in page pc / tpp, slot pc % tpp (tpp = S / 16 <= 64 tiles per page). The quotient
+  // is a multiply-high by a reciprocal fixed per workgroup: with l = ceil(log2 tpp) and
+  // m = ceil(2^(31 + l) / tpp) < 2^32, floor(pc * m / 2^(31 + l)) = floor(pc / tpp) for
+  // 0 <= pc < 2^31, since the product exceeds pc / tpp by less than 2^-l <= 1 / tpp.
+  const int tpp = S / kTile;
+  const int tpp_l = tpp > 1 ? 32 - __builtin_clz((uint32_t)(tpp - 1)) : 0;
+  const uint32_t tpp_m =
+      tpp > 1 ? (uint32_t)((((uint64_t)1 << (31 + tpp_l)) + (uint32_t)tpp - 1) / (uint32_t)tpp) : 0u;
+  auto page_of = [&](int pc) -> int {
+    return tpp > 1 ? (int)(__umulhi((uint32_t)pc, tpp_m) >> (tpp_l - 1)) : pc;
+  };
   auto phys_tile = [&](int v) { return v >= st ? v + shift : v; };
   const int32_t* table_row = a.block_table + (size_t)b * a.max_pages_per_seq;
 
@@ -251,23 +300,25 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
   u32x4 stk[Sh::kLoads];
   u32x4 stv[SHARED ? 1 : Sh::kLoads];
   // Element offset of entry v's tile (page id pid) in a pool, and whether its page is valid.
+  const uint64_t page_elems = (uint64_t)a.num_kv_heads * S * D;  // one page of all KV heads
+  const uint64_t head_elems = (uint64_t)kvh * S * D;              // this KV head within a page
   auto entry_base = [&](int v, int pid, bool& page_ok) -> size_t {
     const int pc = phys_tile(v < t_end ? v : t_last);
     page_ok = (unsigned)pid < (unsigned)a.num_pages;
-    const int pg = page_ok ? pid : 0;
-    const int within = pc - (pc / tiles_per_page) * tiles_per_page;
-    return (((size_t)pg * a.num_kv_heads + kvh) * S + within * kTile) * D;
+    const uint32_t pg = page_ok ? (uint32_t)pid : 0u;
+    const int within = pc - page_of(pc) * tpp;
+    return pg * page_elems + head_elems + (uint32_t)(within * kTile * D);
   };
   auto entry_pid = [&](int v) -> int32_t {
     const int pc = phys_tile(v < t_end ? v : t_last);
-    return load_uniform(table_row, pc / tiles_per_page);
+    return load_uniform(table_row, page_of(pc));
   };
   // Page ids of entries e, e + 1 as a vector (lane u holds entry e + (u & 1)), fetched a step
   // ahead and read back with v_readlane.
   auto pid_vector = [&](int e) -> int32_t {
     const int v = e + (lane & 1);
     const int pc = phys_tile(v < t_end ? v : t_last);
-    return table_row[pc / tiles_per_page];
+    return table_row[page_of(pc)];
   };
   // mats: bit 0 the K tile, bit 1 the V tile (no V tile when SHARED).
   auto issue_loads = [&](int e, int pid0, int pid1, bool* page_ok, int mats, int k_begin = 0,
@@ -324,16 +375,22 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     return full;
   };
 
-  // Direct staging (head_dim 512): wave w fetches key rows 8 w .. 8 w + 7 of the step's two
-  // entries (rows 0-15 entry e, 16-31 entry e + 1), K and V, one instruction per row; lane l
-  // fetches the 16-byte chunk that belongs in slot l of the row (swizzled for K, in order for V).
+  // Direct staging (head_dim 512): wave w fetches key rows kRowsW w .. kRowsW (w + 1) - 1 of the
+  // step's two entries (rows 0-15 entry e, 16-31 entry e + 1), K and V, one instruction per row;
+  // lane l fetches the 16-byte chunk that belongs in slot l of the row (swizzled for K, in order
+  // for V). A wave's rows all belong to one entry, so it needs that entry's address only.
+  constexpr int kRowsW = kStepKeys / kWaves;
+  static_assert(kTile % kRowsW == 0, "a wave's staging rows lie in one entry");
   auto issue_dma = [&](int b2, int e, int pid0, int pid1, bool* page_ok) {
-    const size_t base0 = entry_base(e, pid0, page_ok[0]);
-    const size_t base1 = entry_base(e + 1, pid1, page_ok[1]);
+    const int ent = (kRowsW * wave) / kTile;
+    bool ok_own;
+    const size_t base = entry_base(e + ent, ent ? pid1 : pid0, ok_own);
+    page_ok[0] = (unsigned)pid0 < (unsigned)a.num_pages;
+    page_ok[1] = (unsigned)pid1 < (unsigned)a.num_pages;
 #pragma unroll
-    for (int j = 0; j < kStepKeys / kWaves; ++j) {
-      const int r = (kStepKeys / kWaves) * wave + j;
-      const size_t rb = (r < kTile ? base0 : base1) + (size_t)(r % kTile) * D;
+    for (int j = 0; j < kRowsW; ++j) {
+      const int r = kRowsW * wave + j;
+      const size_t rb = base + (size_t)(r % kTile) * D;
       dma16(a.k_pool + rb + 8 * swz<D>(lane), &KB(b2)[r][0]);
       if constexpr (!SHARED) dma16(a.v_pool + rb + 8 * lane, &VB(b2)[r][0]);
     }
@@ -344,8 +401,8 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     const bool full = entry_full(e, page_ok[0]) && entry_full(e + 1, page_ok[1]);
     if (!full) {
 #pragma unroll
-      for (int j = 0; j < kStepKeys / kWaves; ++j) {
-        const int r = (kStepKeys / kWaves) * wave + j;
+      for (int j = 0; j < kRowsW; ++j) {
+        const int r = kRowsW * wave + j;
         const int v = e + r / kTile;
         const int t = phys_tile(v < t_end ? v : t_last) * kTile + r % kTile;
         const bool in = (v < t_end) & page_ok[r / kTile] & (t < n) & ((t >= lo) | (t < sk));
@@ -418,6 +475,30 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     // for row my_row.
     // The K operands are read kKAhead at a time, all issued before the MFMAs that use them.
     f32x4 sc[2];
+    if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(1);
+    if constexpr (kKPipe > 0 && kDmaD) {
+      // One accumulator per entry, the two entries' MFMAs alternating (MFMA i: entry i % 2,
+      // columns 32 (i / 2) ..); operand i + kKPipe is read right after MFMA i issues, so kKPipe
+      // reads are in flight throughout. Scheduling barriers keep that order.
+      constexpr int kN = 2 * Sh::kQSteps;
+      auto k_read = [&](int i) {
+        return *reinterpret_cast<const bf16x8*>(
+            &KB(buf)[kTile * (i & 1) + col][8 * swz<D>(4 * (i >> 1) + grp)]);
+      };
+      sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+      bf16x8 kb[kKPipeN];
+#pragma unroll
+      for (int i = 0; i < kKPipe; ++i) kb[i] = k_read(i);
+      if (DECODE_ATTN_PREFILL_KPIPE_SB & 2) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kN; ++i) {
+        sc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[i % kKPipeN], qop[i >> 1], sc[i & 1],
+                                                            0, 0, 0);
+        if (i + kKPipe < kN) kb[i % kKPipeN] = k_read(i + kKPipe);
+        if (DECODE_ATTN_PREFILL_KPIPE_SB & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
@@ -445,7 +526,9 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
       }
       sc[g] = p0 + p1;
     }
+    }
 
+    if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(0);
     // Fetch of the tile two steps ahead; it lands during the softmax, P.V and the barrier.
     if constexpr (kEarlyStore) {
       const int pid0 = __builtin_amdgcn_readlane(pid_next, 0);
@@ -524,6 +607,7 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
                       pack_bf16x2(p[1][0], p[1][1]), pack_bf16x2(p[1][2], p[1][3])};
     const bf16x8 pop = __builtin_bit_cast(bf16x8, pa);
 
+    if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(1);
     if constexpr (kTr) {
       // P.V by transpose reads: MFMA e covers output columns 16 e .. 16 e + 15, lane (col, grp)
       // column 16 e + col. Lane col of group grp addresses key row 4 grp + col / 4 (then
@@ -600,6 +684,7 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
       }
     }
 
+    if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(0);
     if constexpr (kDmaD) {  // the next tile has landed in the other buffer: mask its edges
       __builtin_amdgcn_s_waitcnt(0);
       full_nxt = dma_zero(buf ^ 1, e0 + 2, ok_nxt);

@@ -60,6 +60,9 @@ namespace {
 #ifndef DECODE_ATTN_COLS_PER_WAVE_512
 #define DECODE_ATTN_COLS_PER_WAVE_512 128
 #endif
+#ifndef DECODE_ATTN_KV_PAD
+#define DECODE_ATTN_KV_PAD 8
+#endif
 #ifndef DECODE_ATTN_COLS_PER_WAVE_256
 #define DECODE_ATTN_COLS_PER_WAVE_256 64
 #endif
@@ -138,7 +141,7 @@ __global__ __launch_bounds__((Shape<D, RG>::kThreads)) void stage1_kernel(const 
   static_assert(RG == 1 || (RG == 2 && GENERAL), "row groups");
 
   __shared__ __attribute__((aligned(16))) f32x4 score_lds[2][SUB][RG][kWaves][64];
-  constexpr int kKvRow = Sh::kCols + 8;  // padded row of a parked K slice (bf16 elements)
+  constexpr int kKvRow = Sh::kCols + DECODE_ATTN_KV_PAD;  // padded row of a parked K slice (bf16 elements)
   // K in row order through LDS (whole 128-byte lines per load; the A-operand order reads half a
   // line per row per load, which doubles the L2 requests): always for SHARED, and for separate
   // pools with one row group. With two row groups the extra LDS round trip measured slower.

@@ -67,6 +67,10 @@ __device__ __forceinline__ KsRange ks_range(int n, int window) {
   return r;
 }
 
+#ifndef DECODE_ATTN_KS_PAD
+#define DECODE_ATTN_KS_PAD 8
+#endif
+
 // Page ids of this wave's tiles (list entries t0 + NW u for lane u) as a vector: lane u holds the
 // id of the wave's u-th tile from t0 on, the last tile's id past the chunk (never used).
 template <int NW>
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(64 * NW) void stage1_ks_kernel(const Stage1Args a) 
   constexpr int kKsThreads = 64 * NW;
   constexpr bool kValu = DECODE_ATTN_KS_VALU != 0;
   constexpr int kKSteps = D / 32;   // score MFMAs per tile
-  constexpr int kRow = D + 8;       // padded LDS row of a parked K tile (bf16)
+  constexpr int kRow = D + DECODE_ATTN_KS_PAD;       // padded LDS row of a parked K tile (bf16)
   static_assert(G == 1 || G == 2 || G == 4, "group");
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[kValu ? 1 : NW][16][kRow];
   __shared__ __attribute__((aligned(16))) float o_lds[kKsWaves][G][D];
