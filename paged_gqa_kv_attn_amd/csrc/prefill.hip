@@ -284,6 +284,17 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
       qop[c] = __builtin_bit_cast(bf16x8, rv ? v : z);
     }
   }
+  // Scores are scaled by sl2 = |scale * log2 e| (at least FLT_MIN, so that -inf * sl2 stays -inf;
+  // a zero scale then gives scores of 0 up to 1e-38 relative); a negative scale flips the sign of q
+  // instead, so that the softmax can take the maximum of the raw scores and scale it once.
+  const float sl2 = fmaxf(fabsf(a.scale_log2), 1.17549435e-38f);
+  if (a.scale_log2 < 0.f) {
+#pragma unroll
+    for (int c = 0; c < Sh::kQSteps; ++c) {
+      const u32x4 f = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      qop[c] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, qop[c]) ^ f);
+    }
+  }
 
   // Staging of one step's tile (list entries e, e + 1): thread tid loads chunks
   // tid + kThreads * k, i.e. key row k * kKeysPerPass + tid / kChunks, chunk tid % kChunks. The
@@ -341,7 +352,8 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
   // v < t_end, t < n and (t >= lo or t < sk). An entry is full when all its 16 keys are.
   auto entry_full = [&](int v, bool page_ok) {
     const int t0 = phys_tile(v < t_end ? v : t_last) * kTile;
-    return (v < t_end) && page_ok && t0 + kTile <= n && (t0 >= lo || t0 + kTile <= sk);
+    // (Bitwise: every term is cheap, and a chain of short-circuit branches costs more.)
+    return (v < t_end) & page_ok & (t0 + kTile <= n) & ((t0 >= lo) | (t0 + kTile <= sk));
   };
   // Stores the staged tile; keys outside the union are then overwritten with zeros (only entries
   // at the edges of the ranges, or of invalid pages, have any). Returns whether both are full.
@@ -356,7 +368,7 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
       if constexpr (!SHARED)
         if (mats & 2) *reinterpret_cast<u32x4*>(&VB(buf)[ld_key(k)][8 * v_chunk]) = stv[k];
     }
-    const bool full = entry_full(e, page_ok[0]) && entry_full(e + 1, page_ok[1]);
+    const bool full = entry_full(e, page_ok[0]) & entry_full(e + 1, page_ok[1]);
     if (!full) {
 #pragma unroll
       for (int k = 0; k < Sh::kLoads; ++k) {
@@ -398,7 +410,7 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
   // Once this thread's fetches have landed: zeros over the rows it fetched whose key is outside
   // the union (or on an invalid page). Returns whether both entries are full.
   auto dma_zero = [&](int b2, int e, const bool* page_ok) -> bool {
-    const bool full = entry_full(e, page_ok[0]) && entry_full(e + 1, page_ok[1]);
+    const bool full = entry_full(e, page_ok[0]) & entry_full(e + 1, page_ok[1]);
     if (!full) {
 #pragma unroll
       for (int j = 0; j < kRowsW; ++j) {
@@ -551,15 +563,17 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     float mt = -INFINITY;
     const int ta = phys_tile(e0 < t_end ? e0 : t_last) * kTile;
     const int tb = phys_tile(e0 + 1 < t_end ? e0 + 1 : t_last) * kTile;
-    const bool unmasked = full_cur && (ta > tb ? ta : tb) + kTile <= wave_n &&
-                          (ta >= wave_lo || ta + kTile <= sink) &&
-                          (tb >= wave_lo || tb + kTile <= sink);
+    const bool unmasked = full_cur & ((ta > tb ? ta : tb) + kTile <= wave_n) &
+                          ((ta >= wave_lo) | (ta + kTile <= sink)) &
+                          ((tb >= wave_lo) | (tb + kTile <= sink));
+    // s2: the raw scores, -inf where masked; sl2 > 0, so their maximum times sl2 is the maximum of
+    // the scaled scores.
     if (unmasked) {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s2[g][i] = sc[g][i] * a.scale_log2;
+          s2[g][i] = sc[g][i];
           mt = fmaxf(mt, s2[g][i]);
         }
     } else {
@@ -571,12 +585,12 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
         for (int i = 0; i < 4; ++i) {
           const int t = t0 + i;
           const bool att = (v < t_end) & ok_cur[g] & (t < row_n) & ((t >= row_lo) | (t < sink));
-          s2[g][i] = att ? sc[g][i] * a.scale_log2 : -INFINITY;
+          s2[g][i] = att ? sc[g][i] : -INFINITY;
           mt = fmaxf(mt, s2[g][i]);
         }
       }
     }
-    mt = max_xor16_32(mt);
+    mt = max_xor16_32(mt) * sl2;
     const float m_new = fmaxf(m_run, mt);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -586,7 +600,7 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     for (int g = 0; g < 2; ++g)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[g][i] = __builtin_amdgcn_exp2f(s2[g][i] - m_use);
+        p[g][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s2[g][i], sl2, -m_use));
         ps += p[g][i];
       }
     ps = sum_xor16_32(ps);

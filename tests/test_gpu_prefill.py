@@ -175,3 +175,19 @@ def test_prefill_invalid_first_page_is_skipped(D, G, L):
     for splits in (0, 3):
         out, lse = gu.run(inp, force_splits=splits)
         gu.compare(out, lse, *ref, "prefill invalid page D%d G%d L%d ns%d" % (D, G, L, splits))
+
+
+@pytest.mark.parametrize("scale", [-0.06, 0.0])
+@pytest.mark.parametrize("D,G,window", [(512, 8, 0), (512, 2, 0), (256, 4, 300)])
+def test_prefill_negative_and_zero_scale(scale, D, G, window):
+    """A negative scale (the kernel flips q's sign and scales by |scale|, so that the softmax
+    maximum is taken over the raw scores) and a zero scale (uniform weights over the attended
+    keys), on the 128-row kernel (D 512, G 8) and the 64-row ones, with planned and 3 splits."""
+    print("prefill scale=%g D=%d G=%d W=%d" % (scale, D, G, window), flush=True)
+    Hkv = 2
+    inp = make_layer_inputs([130, 700, 1500], G * Hkv, Hkv, D, page_size=16, window=window,
+                            scale=scale, seed=[80, D, G, window, int(scale < 0)], q_len=100)
+    ref = gu.reference(inp)
+    for splits in (0, 3):
+        out, lse = gu.run(inp, force_splits=splits)
+        gu.compare(out, lse, *ref, "prefill scale %g D%d G%d ns%d" % (scale, D, G, splits))
