@@ -30,8 +30,9 @@
 //     pass (measured: no bank conflicts; a 16-byte pad cost about 4 conflict cycles per read).
 //   - scores: S^T[32 keys][16 rows] per wave with v_mfma_f32_16x16x32_bf16, A = K (keys x 32
 //     columns, from LDS), B = the wave's q rows (in registers for the whole kernel). In 128-row
-//     workgroups the operand reads run 4 ahead of the MFMAs (scheduling barriers keep the
-//     compiler from pulling each read down to its MFMA), and both MFMA phases of a step run at
+//     workgroups and at head_dim 256 the operand reads run 4 ahead of the MFMAs (scheduling
+//     barriers keep the compiler from pulling each read down to its MFMA), and in 128-row
+//     workgroups both MFMA phases of a step run at
 //     raised wave priority, so the SIMD's other wave yields its issue slots to them;
 //   - online softmax per row in base 2, exactly as the decode kernel (masks by select, running
 //     max and sum, accumulator rescaled only when a max moved);
@@ -97,7 +98,10 @@ constexpr bool kDma = DECODE_ATTN_PREFILL_DMA;
 #define DECODE_ATTN_PREFILL_KPIPE 4
 #endif
 constexpr int kKPipe = DECODE_ATTN_PREFILL_KPIPE;
-constexpr int kKPipeN = kKPipe > 0 ? kKPipe : 1;  // register slots of the score operand reads
+#ifndef DECODE_ATTN_PREFILL_KPIPE_256
+#define DECODE_ATTN_PREFILL_KPIPE_256 4
+#endif
+constexpr int kKPipe256 = DECODE_ATTN_PREFILL_KPIPE_256;  // the same at head_dim 256 (64 rows)
 #ifndef DECODE_ATTN_PREFILL_KPIPE_SB
 #define DECODE_ATTN_PREFILL_KPIPE_SB 1
 #endif
@@ -182,6 +186,10 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
   constexpr bool kDmaD = kDma && D == 512 && ROWS == kPrefillWideRows;
   constexpr bool kEarlyStore =
       !kDmaD && ((DECODE_ATTN_PREFILL_EARLY_STORE >> (D == 512 ? 0 : 1)) & 1);
+  // Score operand reads in flight (pinned order): 128-row workgroups, and 64-row ones whose score
+  // phase stages nothing (head_dim 256).
+  constexpr int kPipeK = kDmaD ? kKPipe : (!kEarlyStore && D == 256 ? kKPipe256 : 0);
+  constexpr int kPipeKN = kPipeK > 0 ? kPipeK : 1;
   // Score operands read ahead of their MFMAs (fewer when one tile serves as K and V).
   constexpr int kKAhead = SHARED && kDmaD ? DECODE_ATTN_PREFILL_KAHEAD_SHARED
                                            : DECODE_ATTN_PREFILL_KAHEAD;
@@ -488,7 +496,7 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     // The K operands are read kKAhead at a time, all issued before the MFMAs that use them.
     f32x4 sc[2];
     if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(1);
-    if constexpr (kKPipe > 0 && kDmaD) {
+    if constexpr (kPipeK > 0) {
       // One accumulator per entry, the two entries' MFMAs alternating (MFMA i: entry i % 2,
       // columns 32 (i / 2) ..); operand i + kKPipe is read right after MFMA i issues, so kKPipe
       // reads are in flight throughout. Scheduling barriers keep that order.
@@ -499,15 +507,15 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
       };
       sc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
       sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-      bf16x8 kb[kKPipeN];
+      bf16x8 kb[kPipeKN];
 #pragma unroll
-      for (int i = 0; i < kKPipe; ++i) kb[i] = k_read(i);
+      for (int i = 0; i < kPipeK; ++i) kb[i] = k_read(i);
       if (DECODE_ATTN_PREFILL_KPIPE_SB & 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kN; ++i) {
-        sc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[i % kKPipeN], qop[i >> 1], sc[i & 1],
+        sc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[i % kPipeKN], qop[i >> 1], sc[i & 1],
                                                             0, 0, 0);
-        if (i + kKPipe < kN) kb[i % kKPipeN] = k_read(i + kKPipe);
+        if (i + kPipeK < kN) kb[i % kPipeKN] = k_read(i + kPipeK);
         if (DECODE_ATTN_PREFILL_KPIPE_SB & 1) __builtin_amdgcn_sched_barrier(0);
       }
     } else {
