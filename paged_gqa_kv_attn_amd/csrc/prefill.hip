@@ -357,7 +357,18 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     }
   };
   // Key t of entry v is in the union of the block's ranges (read at all) iff its page is valid,
-  // v < t_end, t < n and (t >= lo or t < sk). An entry is full when all its 16 keys are.
+  // v < t_end, t < n and (t >= lo or t < sk). An entry is full when all its 16 keys are. Entries
+  // [0, f_a) (sink tiles of sk keys) and [f_b, f_c) (window tiles from the first one starting at
+  // lo or later) are full whenever their pages are valid. The ranges are conservative (a full
+  // entry outside them takes the exact per-key path) and let a step of the 64-row workgroups test
+  // two integers instead of the per-entry bounds; the 128-row kernel keeps the per-entry tests, with
+  // which the compiler schedules its P.V reads better (measured).
+  const int f_a = min(min(st, sk / kTile), min(n / kTile, t_end));
+  const int f_b = max(st, (lo + kTile - 1) / kTile - shift);
+  const int f_c = min(n / kTile - shift, t_end);
+  auto pair_in = [](int e, int ra, int rb, int rc) {  // entries e and e + 1 in [0, ra) or [rb, rc)
+    return (e + 1 < ra) | ((e >= rb) & (e + 1 < rc));
+  };
   auto entry_full = [&](int v, bool page_ok) {
     const int t0 = phys_tile(v < t_end ? v : t_last) * kTile;
     // (Bitwise: every term is cheap, and a chain of short-circuit branches costs more.)
@@ -376,7 +387,7 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
       if constexpr (!SHARED)
         if (mats & 2) *reinterpret_cast<u32x4*>(&VB(buf)[ld_key(k)][8 * v_chunk]) = stv[k];
     }
-    const bool full = entry_full(e, page_ok[0]) & entry_full(e + 1, page_ok[1]);
+    const bool full = pair_in(e, f_a, f_b, f_c) & page_ok[0] & page_ok[1];
     if (!full) {
 #pragma unroll
       for (int k = 0; k < Sh::kLoads; ++k) {
@@ -447,6 +458,13 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
   }
   wave_n = __builtin_amdgcn_readfirstlane(wave_n);
   wave_lo = __builtin_amdgcn_readfirstlane(wave_lo);
+  // Entries whose keys every existing row of this wave attends, in the form of the full ranges:
+  // sink tiles below sk (<= sink) and n' = min(n, wave_n), window tiles from the first one starting
+  // at max(lo, wave_lo) and ending by n'. A step of two such entries on valid pages needs no mask.
+  const int n_w = min(n, wave_n);
+  const int i_a = min(min(st, sk / kTile), min(n_w / kTile, t_end));
+  const int i_b = max(st, (max(lo, wave_lo) + kTile - 1) / kTile - shift);
+  const int i_c = min(n_w / kTile - shift, t_end);
 
   // Prologue: tile of step 0 into LDS buffer 0, the tile of step 1 in flight.
   bool ok_cur[2], ok_next[2], ok_nxt[2];
@@ -571,9 +589,10 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     float mt = -INFINITY;
     const int ta = phys_tile(e0 < t_end ? e0 : t_last) * kTile;
     const int tb = phys_tile(e0 + 1 < t_end ? e0 + 1 : t_last) * kTile;
-    const bool unmasked = full_cur & ((ta > tb ? ta : tb) + kTile <= wave_n) &
-                          ((ta >= wave_lo) | (ta + kTile <= sink)) &
-                          ((tb >= wave_lo) | (tb + kTile <= sink));
+    const bool unmasked =
+        kDmaD ? full_cur & ((ta > tb ? ta : tb) + kTile <= wave_n) &
+                    ((ta >= wave_lo) | (ta + kTile <= sink)) & ((tb >= wave_lo) | (tb + kTile <= sink))
+              : pair_in(e0, i_a, i_b, i_c) & ok_cur[0] & ok_cur[1];
     // s2: the raw scores, -inf where masked; sl2 > 0, so their maximum times sl2 is the maximum of
     // the scaled scores.
     if (unmasked) {
