@@ -32,10 +32,11 @@
 //     columns, from LDS), B = the wave's q rows (in registers for the whole kernel). In 128-row
 //     workgroups and at head_dim 256 the operand reads run 4 ahead of the MFMAs (scheduling
 //     barriers keep the compiler from pulling each read down to its MFMA), and in 128-row
-//     workgroups both MFMA phases of a step run at
-//     raised wave priority, so the SIMD's other wave yields its issue slots to them;
-//   - online softmax per row in base 2, exactly as the decode kernel (masks by select, running
-//     max and sum, accumulator rescaled only when a max moved);
+//     workgroups both MFMA phases of a step run at raised wave priority, so the SIMD's other wave
+//     yields its issue slots to them;
+//   - online softmax per row in base 2 (masks by select, running max and sum, accumulator
+//     rescaled only when a max moved); the maximum is taken over the raw scores and scaled once,
+//     and each probability is one fma and one exp2;
 //   - P.V with v_mfma_f32_16x16x32_bf16: A = P (16 rows x 32 keys) straight from the score
 //     registers; the 32 keys of the MFMA's reduction run in the order the score layout leaves
 //     them (keys 4g..4g+3 then 16+4g..16+4g+3 for lane group g), and B = V takes its keys in that
