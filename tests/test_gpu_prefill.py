@@ -130,12 +130,14 @@ def test_prefill_workload_global_chunk():
     print("  max_abs_err %.3g  min_cos %.7f" % (err, cos), flush=True)
 
 
-@pytest.mark.parametrize("S", [32, 256, 1024])
+@pytest.mark.parametrize("S", [32, 48, 256, 1008, 1024])
 @pytest.mark.parametrize("D,G,window,sink", [(512, 8, 0, 0), (256, 2, 200, 8)])
 def test_prefill_pages_empty_and_short_sequences(S, D, G, window, sink):
-    """Pages of 32 to 1024 keys (tiles are 16-key slices of a page), an empty sequence (all its
-    queries attend nothing: out = 0, lse = -inf), sequences shorter than the chunk, a window with
-    sinks, and 64 forced splits (most of them empty for the short sequences)."""
+    """Pages of 32 to 1024 keys (tiles are 16-key slices of a page; 48 and 1008 give 3 and 63
+    tiles per page, which the kernel's page-of-tile reciprocal must divide exactly), an empty
+    sequence (all its queries attend nothing: out = 0, lse = -inf), sequences shorter than the
+    chunk, a window with sinks, and 64 forced splits (most of them empty for the short
+    sequences)."""
     print("prefill pages S=%d D=%d G=%d W=%d sink=%d" % (S, D, G, window, sink), flush=True)
     Hkv = 2
     inp = make_layer_inputs([0, 5, 300, 1200], G * Hkv, Hkv, D, page_size=S, window=window,
