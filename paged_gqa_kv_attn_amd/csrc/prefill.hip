@@ -94,7 +94,7 @@ constexpr bool kTr = DECODE_ATTN_PREFILL_TR;
 #endif
 constexpr bool kDma = DECODE_ATTN_PREFILL_DMA;
 // Score operand reads in flight ahead of the MFMAs (128-row workgroups; 0 = the compiler's order,
-// which reads each operand just before its MFMA); KPIPE_SB: bit 0 pins the order.
+// which reads each operand just before its MFMA); KPIPE_SB = 0 leaves the order unpinned.
 #ifndef DECODE_ATTN_PREFILL_KPIPE
 #define DECODE_ATTN_PREFILL_KPIPE 4
 #endif
@@ -517,7 +517,7 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
     if constexpr (kSetPrio) __builtin_amdgcn_s_setprio(1);
     if constexpr (kPipeK > 0) {
       // One accumulator per entry, the two entries' MFMAs alternating (MFMA i: entry i % 2,
-      // columns 32 (i / 2) ..); operand i + kKPipe is read right after MFMA i issues, so kKPipe
+      // columns 32 (i / 2) ..); operand i + kPipeK is read right after MFMA i issues, so kPipeK
       // reads are in flight throughout. Scheduling barriers keep that order.
       constexpr int kN = 2 * Sh::kQSteps;
       auto k_read = [&](int i) {
@@ -529,13 +529,12 @@ __global__ __launch_bounds__(4 * ROWS) void prefill_kernel(const Stage1Args a) {
       bf16x8 kb[kPipeKN];
 #pragma unroll
       for (int i = 0; i < kPipeK; ++i) kb[i] = k_read(i);
-      if (DECODE_ATTN_PREFILL_KPIPE_SB & 2) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < kN; ++i) {
         sc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[i % kPipeKN], qop[i >> 1], sc[i & 1],
                                                             0, 0, 0);
         if (i + kPipeK < kN) kb[i % kPipeKN] = k_read(i + kPipeK);
-        if (DECODE_ATTN_PREFILL_KPIPE_SB & 1) __builtin_amdgcn_sched_barrier(0);
+        if (DECODE_ATTN_PREFILL_KPIPE_SB) __builtin_amdgcn_sched_barrier(0);
       }
     } else {
 #pragma unroll
